@@ -1,0 +1,133 @@
+"""Seeded synthetic inputs for the ParaGRU / ParaLSTM Newton solve.
+
+This module only draws random numbers and lays them out; it holds none of the
+method's arithmetic. Both sides of every parity check (the HIP path and the
+fp64 oracle) consume the tensors it returns, so they see identical bits.
+
+Layouts (shared by the C-ABI and the oracle):
+  u  : [B][L][G][D]  gate pre-activation inputs; GRU gates (z, r, c), LSTM gates
+                     (i, f, o, g); fp32, or bf16 rounded to nearest even.
+  a  : [G][D] fp32   diagonal recurrent coefficients, shared over B and L.
+  dh : [B][L][D] fp32 upstream gradient dL/dh (adjoint workloads only).
+
+Recipe: one CPU torch generator per workload, seeded with the workload's seed;
+draw a = amax * (2 * U[0,1) - 1), then u ~ N(0, 1), then (adjoint only)
+dh ~ N(0, 1), in that order. For the LSTM the forget-gate column gets +1 in
+fp32 before any bf16 rounding. Channels are i.i.d.; a is per channel.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import torch
+
+GATES = {"gru": 3, "lstm": 4}
+NSTATE = {"gru": 1, "lstm": 2}
+LSTM_FORGET_GATE = 1  # gate order (i, f, o, g)
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    cell: str  # "gru" | "lstm"
+    B: int
+    L: int
+    D: int
+    u_dtype: str  # "f32" | "bf16"
+    seed: int
+    amax: float = 1.0
+    forget_bias: float = 0.0
+    adjoint: bool = False
+    iters: int = 3
+
+    @property
+    def G(self) -> int:
+        return GATES[self.cell]
+
+    @property
+    def NS(self) -> int:
+        return NSTATE[self.cell]
+
+    @property
+    def N(self) -> int:
+        return self.B * self.L * self.D
+
+
+# The five workloads the throughput metric and the parity suite are defined on.
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("gru_b1_l1024_d64_f32", "gru", 1, 1024, 64, "f32", seed=0),
+        Workload("gru_b8_l4096_d1024_bf16", "gru", 8, 4096, 1024, "bf16", seed=1),
+        Workload("lstm_b8_l4096_d1024_bf16", "lstm", 8, 4096, 1024, "bf16", seed=2,
+                 forget_bias=1.0),
+        Workload("gru_b1_l65536_d2048_bf16", "gru", 1, 65536, 2048, "bf16", seed=3,
+                 amax=0.9),
+        Workload("lstm_b16_l2048_d4096_bf16_adjoint", "lstm", 16, 2048, 4096, "bf16",
+                 seed=4, adjoint=True),
+    ]
+}
+
+# The workload the headline throughput number is quoted on.
+HEADLINE = "gru_b8_l4096_d1024_bf16"
+
+
+@dataclass
+class Inputs:
+    u: torch.Tensor  # [B][L][G][D], fp32 or bf16, CPU
+    a: torch.Tensor  # [G][D] fp32, CPU
+    dh: Optional[torch.Tensor] = None  # [B][L][D] fp32, CPU
+    meta: dict = field(default_factory=dict)
+
+
+def make_inputs(cell: str, B: int, L: int, D: int, *, seed: int, u_dtype: str = "bf16",
+                amax: float = 1.0, forget_bias: Optional[float] = None,
+                adjoint: bool = False, a_zero: bool = False) -> Inputs:
+    """Draw one seeded input set (see the module docstring for the recipe).
+
+    forget_bias defaults to +1 for the LSTM and 0 for the GRU. a_zero replaces
+    the recurrent coefficients by zeros after drawing them (the draw order, and
+    so u and dh, stay the same), which is the linear-cell special case.
+    """
+    G = GATES[cell]
+    if forget_bias is None:
+        forget_bias = 1.0 if cell == "lstm" else 0.0
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    a = amax * (2.0 * torch.rand(G, D, generator=g, dtype=torch.float32) - 1.0)
+    u = torch.randn(B, L, G, D, generator=g, dtype=torch.float32)
+    if cell == "lstm" and forget_bias != 0.0:
+        u[:, :, LSTM_FORGET_GATE, :] += forget_bias
+    if u_dtype == "bf16":
+        u = u.to(torch.bfloat16)
+    elif u_dtype != "f32":
+        raise ValueError(f"u_dtype must be 'f32' or 'bf16', got {u_dtype!r}")
+    dh = torch.randn(B, L, D, generator=g, dtype=torch.float32) if adjoint else None
+    if a_zero:
+        a = torch.zeros_like(a)
+    return Inputs(u=u.contiguous(), a=a.contiguous(), dh=dh,
+                  meta=dict(cell=cell, B=B, L=L, D=D, seed=seed, u_dtype=u_dtype))
+
+
+def workload_inputs(w: Workload) -> Inputs:
+    return make_inputs(w.cell, w.B, w.L, w.D, seed=w.seed, u_dtype=w.u_dtype, amax=w.amax,
+                       forget_bias=w.forget_bias, adjoint=w.adjoint)
+
+
+def sample_channels(B: int, D: int, n: int, seed: int = 1234) -> torch.Tensor:
+    """n distinct (b, d) channel ids b*D + d, sorted, drawn with their own seed."""
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    n = min(n, B * D)
+    return torch.randperm(B * D, generator=g)[:n].sort().values
+
+
+def gather_channels(x: torch.Tensor, chans: torch.Tensor, D: int) -> torch.Tensor:
+    """Pick channels out of a [B][L][..][D] tensor into a [1][L][..][n] tensor.
+
+    Channels of the diagonal cells never interact, so a gathered sub-problem is
+    solved exactly like the same channels inside the full problem.
+    """
+    b = (chans // D).tolist()
+    d = (chans % D).tolist()
+    cols = [x[bi, ..., di] for bi, di in zip(b, d)]  # each [L] or [L][G]
+    return torch.stack(cols, dim=-1).unsqueeze(0).contiguous()
