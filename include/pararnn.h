@@ -1,0 +1,121 @@
+/*
+ * pararnn.h -- C ABI of the MI355X (gfx950) ParaRNN Newton solver.
+ *
+ * The method (ParaRNN articles, cafecomtech.com "ParaRNN: Apple destrava treino
+ * paralelo de RNNs nao-lineares ..." and aifeed.sk "Apple vracia do hry RNN ..."):
+ * a nonlinear recurrence h_l = f(h_{l-1}, x_l) over a whole sequence is one
+ * system of equations in all hidden states (section "A sacada: metodo de
+ * Newton"). Newton's method linearises it with the per-step Jacobians; the
+ * linearised system is a linear SSM h_l = A_l h_{l-1} + b_l with the Jacobians
+ * as A_l, solved by a parallel scan (section "O compromisso que SSMs fizeram").
+ * With diagonal cell matrices the Jacobians are diagonal (ParaGRU) or 2x2
+ * block-diagonal over (c, h) (ParaLSTM) (section "Engenharia pra escalar").
+ *
+ * Cells, per channel d, with gate inputs u precomputed and diagonal recurrent
+ * coefficients a (s = logistic sigmoid):
+ *   GRU,  gates (z, r, c):  z = s(a_z h + u_z), r = s(a_r h + u_r),
+ *         c~ = tanh(a_c (r h) + u_c), h' = (1 - z) h + z c~.
+ *   LSTM, gates (i, f, o, g), state (c, h): i, f, o = s(a_* h + u_*),
+ *         g = tanh(a_g h + u_g), c' = f c + i g, h' = o tanh(c').
+ *
+ * Conventions for every call:
+ *  - All array pointers are DEVICE pointers to caller-owned, contiguous,
+ *    row-major buffers. The library never allocates, frees or keeps a pointer
+ *    after returning; all scratch lives in the caller's workspace `ws`.
+ *  - Layouts: u [B][L][G][D] (fp32 or bf16 per opts.u_dtype), a [G][D] fp32,
+ *    states h, c [B][L][D] fp32, initial states h0, c0 [B][D] fp32 (NULL means
+ *    zero), dh [B][L][D] fp32, du [B][L][G][D] fp32 (always fp32).
+ *  - Pointers must be at least 4-byte aligned (2-byte for bf16 u); 16-byte
+ *    alignment with D divisible by 4 selects the widest memory accesses.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Calls are
+ *    asynchronous: inputs must stay alive and unmodified, and outputs must not
+ *    be read, until the stream reaches the end of the call. Calls on different
+ *    streams are safe when each has its own workspace; two calls sharing one
+ *    workspace must be ordered on one stream.
+ *  - Inputs and outputs must not alias each other or the workspace.
+ *  - Return value: PARARNN_OK, or a negative PARARNN_E* code; on an error
+ *    nothing has been launched (except PARARNN_EHIP, reported when a launch
+ *    itself fails). Numerical trouble is not an error: NaN/Inf propagate into
+ *    the states and max_update, and the row is reported as not converged.
+ */
+#ifndef PARARNN_H
+#define PARARNN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PARARNN_OK 0
+#define PARARNN_EINVAL (-1)       /* null pointer, size <= 0, max_iters < 1, bad enum, size overflow */
+#define PARARNN_EUNSUPPORTED (-2) /* unsupported dtype or misaligned pointer */
+#define PARARNN_EWORKSPACE (-3)   /* ws_bytes smaller than pararnn_workspace_bytes() */
+#define PARARNN_EHIP (-4)         /* a HIP launch or runtime call failed */
+
+typedef enum { PARARNN_F32 = 0, PARARNN_BF16 = 1 } pararnn_dtype;
+typedef enum { PARARNN_GRU = 0, PARARNN_LSTM = 1 } pararnn_cell;
+typedef enum { PARARNN_OP_SOLVE = 0, PARARNN_OP_ADJOINT = 1 } pararnn_op;
+
+typedef struct {
+  int32_t B, L, D;    /* batch rows, sequence length, channels; all >= 1 */
+  int32_t max_iters;  /* K: Newton iterations (launches), >= 1 */
+  float tol;          /* convergence threshold on max |update| of the last iteration */
+  int32_t early_exit; /* 0: always K iterations. 1: stop after the first iteration
+                         whose update satisfies tol on every row (later launches copy) */
+  int32_t u_dtype;    /* pararnn_dtype of u */
+  void* const* events; /* optional: K + 2 hipEvent_t handles recorded on `stream`
+                          before the workspace reset, after it, and after each
+                          iteration (solve) / the adjoint launch (adjoint: 3 events);
+                          NULL = none */
+} pararnn_opts;
+
+/* Bytes of workspace a call with these options needs (depends on the cell,
+ * the operation, B, L, D, max_iters and u_dtype). Returns 0 for invalid
+ * options. Host-only; launches nothing. */
+size_t pararnn_workspace_bytes(int32_t cell, int32_t op, const pararnn_opts* o);
+
+/* ParaGRU forward solve: K Newton iterations from the zero sequence (the
+ * initial state h0 is fixed). Iteration k linearises the system at iterate k-1,
+ * assembles the diagonal Jacobian coefficients and solves the linear SSM by a
+ * parallel scan, in one fused launch. Outputs (device):
+ *   h          [B][L][D] the K-th iterate (always; also with early exit)
+ *   iters      [1] number of iterations performed (K unless early exit fired), or NULL
+ *   converged  [B] 1 if max |h^(iters) - h^(iters-1)| <= tol on that row, else 0, or NULL
+ *   max_update [K][B] max |h^(k) - h^(k-1)| per iteration and row (0 for skipped
+ *              iterations; NaN if the row holds NaN), or NULL */
+int32_t pararnn_solve_gru(const void* u, const float* a, const float* h0, float* h, void* ws,
+                          size_t ws_bytes, const pararnn_opts* o, int32_t* iters,
+                          int32_t* converged, float* max_update, void* stream);
+
+/* ParaLSTM forward solve: as pararnn_solve_gru with the 2x2 block Jacobian over
+ * (c, h). Outputs c and h, both [B][L][D]; max_update is the max over both
+ * state components. */
+int32_t pararnn_solve_lstm(const void* u, const float* a, const float* c0, const float* h0,
+                           float* c, float* h, void* ws, size_t ws_bytes, const pararnn_opts* o,
+                           int32_t* iters, int32_t* converged, float* max_update, void* stream);
+
+/* Adjoint (reverse linear scan) along a given trajectory, e.g. the solve's
+ * output, for upstream gradient dh = dL/dh:
+ *   lambda_{L-1} = G_{L-1},  lambda_l = G_l + J_{l+1}^T lambda_{l+1},
+ *   J_{l+1} = df/ds at (state_l, u_{l+1}), G_l = dh_l (GRU) or (0, dh_l) (LSTM),
+ *   du_l = (df/du at (state_{l-1}, u_l))^T lambda_l.
+ * c and c0 are ignored for the GRU (pass NULL). Outputs (device, fp32):
+ *   du  [B][L][G][D]
+ *   ds0 [NS][B][D] gradient of the initial state (NS = 1: h0; NS = 2: c0 then h0), or NULL
+ *   da  [G][D] gradient of the coefficients summed over B and L, or NULL
+ * opts.max_iters, tol and early_exit are ignored. */
+int32_t pararnn_adjoint(int32_t cell, const void* u, const float* a, const float* c0,
+                        const float* h0, const float* c, const float* h, const float* dh,
+                        float* du, float* ds0, float* da, void* ws, size_t ws_bytes,
+                        const pararnn_opts* o, void* stream);
+
+/* Static description of a status code. */
+const char* pararnn_strerror(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PARARNN_H */

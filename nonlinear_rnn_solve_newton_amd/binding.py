@@ -1,0 +1,223 @@
+"""Thin Python binding of libpararnn.so (argument marshalling only).
+
+Every step of the solve runs in the HIP library; this module only checks
+tensor placement, allocates outputs and workspace with torch, and passes raw
+device pointers plus torch's current HIP stream through ctypes. There is no
+fallback: if the library is missing or the tensors are not on a ROCm device,
+the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import re
+from pathlib import Path
+from typing import Optional, Sequence
+
+import torch
+
+PKG = Path(__file__).resolve().parent
+LIB_PATH = PKG / "libpararnn.so"
+HEADER = PKG.parent / "include" / "pararnn.h"
+
+GRU, LSTM = 0, 1
+OP_SOLVE, OP_ADJOINT = 0, 1
+F32, BF16 = 0, 1
+CELLS = {"gru": GRU, "lstm": LSTM}
+GATES = {"gru": 3, "lstm": 4}
+NSTATE = {"gru": 1, "lstm": 2}
+
+
+class PararnnError(RuntimeError):
+    pass
+
+
+class Opts(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32),
+        ("L", ctypes.c_int32),
+        ("D", ctypes.c_int32),
+        ("max_iters", ctypes.c_int32),
+        ("tol", ctypes.c_float),
+        ("early_exit", ctypes.c_int32),
+        ("u_dtype", ctypes.c_int32),
+        ("events", ctypes.c_void_p),
+    ]
+
+
+def header_functions() -> list[str]:
+    """Names of the functions declared in include/pararnn.h."""
+    text = HEADER.read_text()
+    return re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?(pararnn_[a-z_]+)\s*\(", text, re.M)
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise PararnnError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        L = ctypes.CDLL(str(LIB_PATH))
+        P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        OPTP = ctypes.POINTER(Opts)
+        L.pararnn_workspace_bytes.argtypes = [I32, I32, OPTP]
+        L.pararnn_workspace_bytes.restype = SZ
+        L.pararnn_solve_gru.argtypes = [P, P, P, P, P, SZ, OPTP, P, P, P, P]
+        L.pararnn_solve_gru.restype = I32
+        L.pararnn_solve_lstm.argtypes = [P, P, P, P, P, P, P, SZ, OPTP, P, P, P, P]
+        L.pararnn_solve_lstm.restype = I32
+        L.pararnn_adjoint.argtypes = [I32, P, P, P, P, P, P, P, P, P, P, P, SZ, OPTP, P]
+        L.pararnn_adjoint.restype = I32
+        L.pararnn_strerror.argtypes = [I32]
+        L.pararnn_strerror.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().pararnn_strerror(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise PararnnError(f"{what} failed: {status} ({strerror(status)})")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise PararnnError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise PararnnError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise PararnnError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise PararnnError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _u_dtype(u: torch.Tensor) -> int:
+    if u.dtype == torch.float32:
+        return F32
+    if u.dtype == torch.bfloat16:
+        return BF16
+    raise PararnnError(f"u must be float32 or bfloat16, got {u.dtype}")
+
+
+def make_opts(B, L, D, iters=3, tol=1e-4, early_exit=False, u_dtype=BF16, events=None):
+    o = Opts(B, L, D, iters, tol, int(bool(early_exit)), u_dtype, None)
+    keep = None
+    if events is not None:
+        keep = (ctypes.c_void_p * len(events))(*events)
+        o.events = ctypes.cast(keep, ctypes.c_void_p)
+    return o, keep
+
+
+def workspace_bytes(cell: str, op: int, B: int, L: int, D: int, iters: int = 3,
+                    u_dtype: int = BF16) -> int:
+    o, _ = make_opts(B, L, D, iters, 1e-4, False, u_dtype)
+    return int(lib().pararnn_workspace_bytes(CELLS[cell], op, ctypes.byref(o)))
+
+
+def alloc_workspace(nbytes: int, device) -> torch.Tensor:
+    # torch's caching allocator returns 512-byte aligned blocks
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def solve(cell: str, u: torch.Tensor, a: torch.Tensor, *, h0=None, c0=None, iters: int = 3,
+          tol: float = 1e-4, early_exit: bool = False, ws: Optional[torch.Tensor] = None,
+          out=None, events: Optional[Sequence[int]] = None):
+    """Newton solve; returns dict(h, c (LSTM), iters, converged, max_update) on u's device."""
+    G, NS = GATES[cell], NSTATE[cell]
+    _dev(u, "u")
+    if u.dim() != 4 or u.shape[2] != G:
+        raise PararnnError(f"u must be [B][L][{G}][D]")
+    B, L, _, D = u.shape
+    dev = u.device
+    _dev(a, "a", torch.float32, (G, D))
+    _dev(h0, "h0", torch.float32, (B, D))
+    _dev(c0, "c0", torch.float32, (B, D))
+    udt = _u_dtype(u)
+    if out is None:
+        out = {"h": torch.empty(B, L, D, dtype=torch.float32, device=dev)}
+        if NS == 2:
+            out["c"] = torch.empty(B, L, D, dtype=torch.float32, device=dev)
+    for k in out:
+        _dev(out[k], k, torch.float32, (B, L, D))
+    it = torch.empty(1, dtype=torch.int32, device=dev)
+    conv = torch.empty(B, dtype=torch.int32, device=dev)
+    mu = torch.empty(iters, B, dtype=torch.float32, device=dev)
+    o, keep = make_opts(B, L, D, iters, tol, early_exit, udt, events)
+    need = int(lib().pararnn_workspace_bytes(CELLS[cell], OP_SOLVE, ctypes.byref(o)))
+    if need == 0:
+        raise PararnnError("invalid sizes or iteration count")
+    if ws is None:
+        ws = alloc_workspace(need, dev)
+    if cell == "gru":
+        st = lib().pararnn_solve_gru(_ptr(u), _ptr(a), _ptr(h0), _ptr(out["h"]), _ptr(ws), ws.numel(),
+                                     ctypes.byref(o), _ptr(it), _ptr(conv), _ptr(mu), _stream(dev))
+    else:
+        st = lib().pararnn_solve_lstm(_ptr(u), _ptr(a), _ptr(c0), _ptr(h0), _ptr(out["c"]), _ptr(out["h"]),
+                                      _ptr(ws), ws.numel(), ctypes.byref(o), _ptr(it), _ptr(conv),
+                                      _ptr(mu), _stream(dev))
+    del keep
+    _check(st, f"pararnn_solve_{cell}")
+    res = dict(out)
+    res.update(iters=it, converged=conv, max_update=mu, ws=ws)
+    return res
+
+
+def solve_gru(u, a, h0=None, **kw):
+    return solve("gru", u, a, h0=h0, **kw)
+
+
+def solve_lstm(u, a, c0=None, h0=None, **kw):
+    return solve("lstm", u, a, h0=h0, c0=c0, **kw)
+
+
+def adjoint(cell: str, u: torch.Tensor, a: torch.Tensor, h: torch.Tensor, dh: torch.Tensor, *,
+            c=None, h0=None, c0=None, want_ds0: bool = False, want_da: bool = False,
+            ws: Optional[torch.Tensor] = None, du: Optional[torch.Tensor] = None,
+            events: Optional[Sequence[int]] = None):
+    """Reverse scan along the trajectory (c, h); returns dict(du, ds0, da)."""
+    G, NS = GATES[cell], NSTATE[cell]
+    _dev(u, "u")
+    if u.dim() != 4 or u.shape[2] != G:
+        raise PararnnError(f"u must be [B][L][{G}][D]")
+    B, L, _, D = u.shape
+    dev = u.device
+    _dev(a, "a", torch.float32, (G, D))
+    _dev(h, "h", torch.float32, (B, L, D))
+    _dev(c, "c", torch.float32, (B, L, D))
+    _dev(dh, "dh", torch.float32, (B, L, D))
+    _dev(h0, "h0", torch.float32, (B, D))
+    _dev(c0, "c0", torch.float32, (B, D))
+    if NS == 2 and c is None:
+        raise PararnnError("the LSTM adjoint needs the c trajectory")
+    if du is None:
+        du = torch.empty(B, L, G, D, dtype=torch.float32, device=dev)
+    _dev(du, "du", torch.float32, (B, L, G, D))
+    ds0 = torch.empty(NS, B, D, dtype=torch.float32, device=dev) if want_ds0 else None
+    da = torch.empty(G, D, dtype=torch.float32, device=dev) if want_da else None
+    o, keep = make_opts(B, L, D, 1, 0.0, False, _u_dtype(u), events)
+    need = int(lib().pararnn_workspace_bytes(CELLS[cell], OP_ADJOINT, ctypes.byref(o)))
+    if need == 0:
+        raise PararnnError("invalid sizes")
+    if ws is None:
+        ws = alloc_workspace(need, dev)
+    st = lib().pararnn_adjoint(CELLS[cell], _ptr(u), _ptr(a), _ptr(c0), _ptr(h0), _ptr(c), _ptr(h), _ptr(dh),
+                               _ptr(du), _ptr(ds0), _ptr(da), _ptr(ws), ws.numel(), ctypes.byref(o),
+                               _stream(dev))
+    del keep
+    _check(st, "pararnn_adjoint")
+    return dict(du=du, ds0=ds0, da=da, ws=ws)

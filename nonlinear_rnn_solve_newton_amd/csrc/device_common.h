@@ -1,0 +1,302 @@
+// device_common.h -- numerics, vector memory access, the two cells and the
+// chunk-carry descriptors shared by the Newton-iteration and adjoint kernels.
+// gfx950 (CDNA4) only: wave64, v_exp_f32 / v_rcp_f32, agent-scope atomics.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pararnn {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Storage tag for bfloat16 gate inputs (raw bits; widened to fp32 exactly).
+struct bf16 {
+  uint16_t bits;
+};
+
+// ---------------------------------------------------------------------------
+// numerics: logistic sigmoid from the hardware base-2 exponential and
+// reciprocal (about 1 ulp each); tanh(x) = 2 s(2x) - 1. Overflow of the
+// exponential gives the correct limits (s -> 0 or 1); NaN propagates.
+__device__ __forceinline__ float sigm(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.4426950408889634f));
+}
+__device__ __forceinline__ float tanh_fast(float x) { return fmaf(2.0f, sigm(2.0f * x), -1.0f); }
+
+// ---------------------------------------------------------------------------
+// vector loads / stores of C consecutive channels (C in {1, 2, 4}); the host
+// only selects C when every pointer and row offset is aligned for it.
+template <int C>
+__device__ __forceinline__ void ld_f32(const float* p, float (&v)[C]) {
+  if constexpr (C == 4) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(p);
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  } else if constexpr (C == 2) {
+    const f32x2 x = *reinterpret_cast<const f32x2*>(p);
+    v[0] = x.x; v[1] = x.y;
+  } else {
+    v[0] = *p;
+  }
+}
+
+template <int C>
+__device__ __forceinline__ void st_f32(float* p, const float (&v)[C]) {
+  if constexpr (C == 4) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+  } else if constexpr (C == 2) {
+    *reinterpret_cast<f32x2*>(p) = f32x2{v[0], v[1]};
+  } else {
+    *p = v[0];
+  }
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Raw gate-input registers: bf16 inputs stay packed (two per 32-bit
+// register) until the cell evaluation widens them, which halves the registers
+// held while the loads are in flight.
+template <class UT, int C>
+struct URaw;
+
+template <int C>
+struct URaw<float, C> {
+  float v[C];
+  __device__ __forceinline__ void load(const float* p) { ld_f32<C>(p, v); }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int c = 0; c < C; ++c) v[c] = 0.0f;
+  }
+  __device__ __forceinline__ float get(int c) const { return v[c]; }
+};
+
+template <int C>
+struct URaw<bf16, C> {
+  static constexpr int NW = (C + 1) / 2;
+  uint32_t w[NW];
+  __device__ __forceinline__ void load(const bf16* p) {
+    if constexpr (C == 4) {
+      const u32x2 x = *reinterpret_cast<const u32x2*>(p);
+      w[0] = x.x;
+      w[1] = x.y;
+    } else if constexpr (C == 2) {
+      w[0] = *reinterpret_cast<const uint32_t*>(p);
+    } else {
+      w[0] = static_cast<uint32_t>(p->bits);
+    }
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) w[i] = 0u;
+  }
+  __device__ __forceinline__ float get(int c) const {
+    return (c & 1) ? bf16_hi(w[c >> 1]) : bf16_lo(w[c >> 1]);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Cells. step() evaluates the next state f and its Jacobian J = df/ds at the
+// previous state s; step_adj() also returns dfdu = df/du and the multiplier
+// m of each coefficient in its gate pre-activation (df/da_g = dfdu[.][g] * m_g).
+// ParaGRU: diagonal Jacobian (1x1 per channel); ParaLSTM: 2x2 over (c, h),
+// per the ParaRNN article's section "Engenharia pra escalar".
+struct GruCell {
+  static constexpr int NS = 1;  // state: h
+  static constexpr int G = 3;   // gates: z, r, c
+
+  __device__ static __forceinline__ void step(const float (&a)[G], const float (&u)[G],
+                                              const float (&s)[NS], float (&f)[NS],
+                                              float (&J)[NS][NS]) {
+    const float h = s[0];
+    const float z = sigm(fmaf(a[0], h, u[0]));
+    const float r = sigm(fmaf(a[1], h, u[1]));
+    const float c = tanh_fast(fmaf(a[2], r * h, u[2]));
+    const float cmh = c - h;
+    f[0] = fmaf(z, cmh, h);  // (1 - z) h + z c
+    const float omz = 1.0f - z;
+    const float gz = cmh * z * omz;            // df / d pre_z
+    const float gc = z * fmaf(-c, c, 1.0f);    // df / d pre_c
+    const float drh = fmaf(h * a[1], r - r * r, r);  // d (r h) / dh
+    J[0][0] = fmaf(gc * a[2], drh, fmaf(gz, a[0], omz));
+  }
+
+  __device__ static __forceinline__ void step_adj(const float (&a)[G], const float (&u)[G],
+                                                  const float (&s)[NS], float (&J)[NS][NS],
+                                                  float (&dfdu)[NS][G], float (&m)[G]) {
+    const float h = s[0];
+    const float z = sigm(fmaf(a[0], h, u[0]));
+    const float r = sigm(fmaf(a[1], h, u[1]));
+    const float rh = r * h;
+    const float c = tanh_fast(fmaf(a[2], rh, u[2]));
+    const float cmh = c - h;
+    const float omz = 1.0f - z;
+    const float gz = cmh * z * omz;
+    const float gc = z * fmaf(-c, c, 1.0f);
+    const float rr = r - r * r;
+    const float drh = fmaf(h * a[1], rr, r);
+    J[0][0] = fmaf(gc * a[2], drh, fmaf(gz, a[0], omz));
+    dfdu[0][0] = gz;
+    dfdu[0][1] = gc * a[2] * h * rr;
+    dfdu[0][2] = gc;
+    m[0] = h;
+    m[1] = h;
+    m[2] = rh;
+  }
+};
+
+struct LstmCell {
+  static constexpr int NS = 2;  // state: (c, h)
+  static constexpr int G = 4;   // gates: i, f, o, g
+
+  __device__ static __forceinline__ void step(const float (&a)[G], const float (&u)[G],
+                                              const float (&s)[NS], float (&f)[NS],
+                                              float (&J)[NS][NS]) {
+    const float cp = s[0], hp = s[1];
+    const float gi = sigm(fmaf(a[0], hp, u[0]));
+    const float gf = sigm(fmaf(a[1], hp, u[1]));
+    const float go = sigm(fmaf(a[2], hp, u[2]));
+    const float gg = tanh_fast(fmaf(a[3], hp, u[3]));
+    const float cn = fmaf(gf, cp, gi * gg);
+    const float t = tanh_fast(cn);
+    f[0] = cn;
+    f[1] = go * t;
+    const float dci = gg * (gi - gi * gi);
+    const float dcf = cp * (gf - gf * gf);
+    const float dcg = gi * fmaf(-gg, gg, 1.0f);
+    const float q = go * fmaf(-t, t, 1.0f);  // dh'/dc'
+    const float dho = t * (go - go * go);
+    const float X = fmaf(dci, a[0], fmaf(dcf, a[1], dcg * a[3]));  // dc'/dh
+    J[0][0] = gf;
+    J[0][1] = X;
+    J[1][0] = q * gf;
+    J[1][1] = fmaf(dho, a[2], q * X);
+  }
+
+  __device__ static __forceinline__ void step_adj(const float (&a)[G], const float (&u)[G],
+                                                  const float (&s)[NS], float (&J)[NS][NS],
+                                                  float (&dfdu)[NS][G], float (&m)[G]) {
+    const float cp = s[0], hp = s[1];
+    const float gi = sigm(fmaf(a[0], hp, u[0]));
+    const float gf = sigm(fmaf(a[1], hp, u[1]));
+    const float go = sigm(fmaf(a[2], hp, u[2]));
+    const float gg = tanh_fast(fmaf(a[3], hp, u[3]));
+    const float cn = fmaf(gf, cp, gi * gg);
+    const float t = tanh_fast(cn);
+    const float dci = gg * (gi - gi * gi);
+    const float dcf = cp * (gf - gf * gf);
+    const float dcg = gi * fmaf(-gg, gg, 1.0f);
+    const float q = go * fmaf(-t, t, 1.0f);
+    const float dho = t * (go - go * go);
+    const float X = fmaf(dci, a[0], fmaf(dcf, a[1], dcg * a[3]));
+    J[0][0] = gf;
+    J[0][1] = X;
+    J[1][0] = q * gf;
+    J[1][1] = fmaf(dho, a[2], q * X);
+    dfdu[0][0] = dci; dfdu[0][1] = dcf; dfdu[0][2] = 0.0f; dfdu[0][3] = dcg;
+    dfdu[1][0] = q * dci; dfdu[1][1] = q * dcf; dfdu[1][2] = dho; dfdu[1][3] = q * dcg;
+    m[0] = hp; m[1] = hp; m[2] = hp; m[3] = hp;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Chunk-carry descriptors for the decoupled look-back across workgroups.
+// Every value travels in its own 64-bit word: high half = tag (the Newton
+// iteration number, >= 1; 0 = not yet written in this call), low half = the
+// fp32 bits. A word is written once per launch with a relaxed agent-scope
+// atomic store and polled with relaxed agent-scope atomic loads, so a reader
+// either sees the old tag or the complete new value; no fences are needed
+// and no value can be mistaken for another launch's.
+__device__ __forceinline__ void desc_put(unsigned long long* p, uint32_t tag, float v) {
+  const unsigned long long w = (static_cast<unsigned long long>(tag) << 32) | __float_as_uint(v);
+  __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long desc_get(unsigned long long* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool desc_ok(unsigned long long w, uint32_t tag) {
+  return static_cast<uint32_t>(w >> 32) == tag;
+}
+__device__ __forceinline__ float desc_val(unsigned long long w) {
+  return __uint_as_float(static_cast<uint32_t>(w));
+}
+
+// ---------------------------------------------------------------------------
+// Affine scan element over NS-vectors for C channels: x -> A x + b.
+template <int NS, int C>
+struct Aff {
+  float A[NS][NS][C];
+  float b[NS][C];
+
+  __device__ __forceinline__ void set_identity() {
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+#pragma unroll
+      for (int j = 0; j < NS; ++j)
+#pragma unroll
+        for (int c = 0; c < C; ++c) A[i][j][c] = (i == j) ? 1.0f : 0.0f;
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+#pragma unroll
+      for (int c = 0; c < C; ++c) b[i][c] = 0.0f;
+  }
+
+  // this <- this o e  (apply e first, then this)
+  __device__ __forceinline__ void after(const Aff& e) {
+    Aff r;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+          float acc = 0.0f;
+#pragma unroll
+          for (int k = 0; k < NS; ++k) acc = fmaf(A[i][k][c], e.A[k][j][c], acc);
+          r.A[i][j][c] = acc;
+        }
+        float acc = b[i][c];
+#pragma unroll
+        for (int k = 0; k < NS; ++k) acc = fmaf(A[i][k][c], e.b[k][c], acc);
+        r.b[i][c] = acc;
+      }
+    }
+    *this = r;
+  }
+
+  // y = A x + b on vectors x[NS][C]
+  __device__ __forceinline__ void apply(float (&x)[NS][C]) const {
+    float y[NS][C];
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        float acc = b[i][c];
+#pragma unroll
+        for (int k = 0; k < NS; ++k) acc = fmaf(A[i][k][c], x[k][c], acc);
+        y[i][c] = acc;
+      }
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int i = 0; i < NS; ++i) x[i][c] = y[i][c];
+  }
+
+  // wave shuffle: value of the lane `delta` below (same value kept on lanes < delta)
+  __device__ __forceinline__ Aff shfl_up(int delta) const {
+    Aff r;
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+#pragma unroll
+        for (int j = 0; j < NS; ++j) r.A[i][j][c] = __shfl_up(A[i][j][c], delta, 64);
+        r.b[i][c] = __shfl_up(b[i][c], delta, 64);
+      }
+    return r;
+  }
+};
+
+}  // namespace pararnn

@@ -1,0 +1,346 @@
+// pararnn.hip -- host side of the C ABI declared in include/pararnn.h:
+// argument validation, launch-configuration choice, workspace carving and the
+// launch sequence (workspace reset, then one fused launch per Newton iteration,
+// or one adjoint launch), all asynchronous on the caller's stream.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/pararnn.h"
+#include "adjoint.h"
+#include "newton_iter.h"
+
+namespace pararnn {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Launch configurations. Per (cell, C): T timesteps per lane, W waves per
+// workgroup, LL lane groups along L per wave. The chunk length W*LL*T is fixed
+// per cell and operation so that the workspace size does not depend on C.
+template <class Cell, int C, bool ADJ>
+struct Cfg;
+// ParaGRU forward: chunk 128 timesteps
+template <> struct Cfg<GruCell, 4, false> { static constexpr int T = 8, W = 4, LL = 4; };
+template <> struct Cfg<GruCell, 2, false> { static constexpr int T = 8, W = 8, LL = 2; };
+template <> struct Cfg<GruCell, 1, false> { static constexpr int T = 16, W = 8, LL = 1; };
+// ParaLSTM forward: chunk 128
+template <> struct Cfg<LstmCell, 4, false> { static constexpr int T = 4, W = 8, LL = 4; };
+template <> struct Cfg<LstmCell, 2, false> { static constexpr int T = 8, W = 4, LL = 4; };
+template <> struct Cfg<LstmCell, 1, false> { static constexpr int T = 16, W = 8, LL = 1; };
+// adjoints: chunk 128
+template <> struct Cfg<GruCell, 4, true> { static constexpr int T = 4, W = 8, LL = 4; };
+template <> struct Cfg<GruCell, 2, true> { static constexpr int T = 8, W = 4, LL = 4; };
+template <> struct Cfg<GruCell, 1, true> { static constexpr int T = 8, W = 8, LL = 2; };
+template <> struct Cfg<LstmCell, 4, true> { static constexpr int T = 4, W = 8, LL = 4; };
+template <> struct Cfg<LstmCell, 2, true> { static constexpr int T = 4, W = 8, LL = 4; };
+template <> struct Cfg<LstmCell, 1, true> { static constexpr int T = 8, W = 8, LL = 2; };
+
+constexpr int kChunk = 128;
+
+template <class Cell, int C, bool ADJ>
+constexpr int chunk_len() {
+  return Cfg<Cell, C, ADJ>::T * Cfg<Cell, C, ADJ>::W * Cfg<Cell, C, ADJ>::LL;
+}
+static_assert(chunk_len<GruCell, 4, false>() == kChunk && chunk_len<GruCell, 2, false>() == kChunk &&
+                  chunk_len<GruCell, 1, false>() == kChunk && chunk_len<LstmCell, 4, false>() == kChunk &&
+                  chunk_len<LstmCell, 2, false>() == kChunk && chunk_len<LstmCell, 1, false>() == kChunk &&
+                  chunk_len<GruCell, 4, true>() == kChunk && chunk_len<GruCell, 2, true>() == kChunk &&
+                  chunk_len<GruCell, 1, true>() == kChunk && chunk_len<LstmCell, 4, true>() == kChunk &&
+                  chunk_len<LstmCell, 2, true>() == kChunk && chunk_len<LstmCell, 1, true>() == kChunk,
+              "every configuration must cover kChunk timesteps per workgroup");
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  size_t ctr = 0, maxupd = 0, incl = 0, agg = 0, dapart = 0, zero_end = 0, state = 0, total = 0;
+  int nchunks = 0;
+};
+
+int nstate(int cell) { return cell == PARARNN_LSTM ? 2 : 1; }
+int ngates(int cell) { return cell == PARARNN_LSTM ? 4 : 3; }
+
+bool opts_ok(int cell, int op, const pararnn_opts* o) {
+  if (!o) return false;
+  if (cell != PARARNN_GRU && cell != PARARNN_LSTM) return false;
+  if (op != PARARNN_OP_SOLVE && op != PARARNN_OP_ADJOINT) return false;
+  if (o->B < 1 || o->L < 1 || o->D < 1) return false;
+  if (op == PARARNN_OP_SOLVE && (o->max_iters < 1 || o->max_iters > 1000)) return false;
+  // element counts must stay addressable with 64-bit offsets and tickets in 32 bits
+  const double n = static_cast<double>(o->B) * o->L * o->D * 4;
+  if (n > 9.0e18) return false;
+  const double wgs = static_cast<double>(o->B) * ((o->D + 15) / 16) * ((o->L + kChunk - 1) / kChunk);
+  if (wgs > 2.0e9) return false;
+  return true;
+}
+
+// Workspace: [counters | row maxima | incl descriptors | agg descriptors | da partials]
+// (cleared at the start of every call) followed by the ping-pong state buffer.
+Layout layout(int cell, int op, const pararnn_opts* o, bool with_da) {
+  Layout y;
+  const int NS = nstate(cell), G = ngates(cell);
+  const size_t B = o->B, L = o->L, D = o->D;
+  const int K = (op == PARARNN_OP_SOLVE) ? o->max_iters : 1;
+  y.nchunks = static_cast<int>((L + kChunk - 1) / kChunk);
+  size_t off = 0;
+  y.ctr = off;
+  off = round_up(off + sizeof(uint32_t) * (2 * K + 1));
+  y.maxupd = off;
+  off = round_up(off + sizeof(uint32_t) * static_cast<size_t>(K) * B);
+  y.incl = off;
+  if (y.nchunks > 1) off = round_up(off + sizeof(uint64_t) * y.nchunks * NS * B * D);
+  y.agg = off;
+  if (y.nchunks > 1) off = round_up(off + sizeof(uint64_t) * y.nchunks * (NS * NS + NS) * B * D);
+  y.zero_end = off;
+  y.dapart = off;
+  if (op == PARARNN_OP_ADJOINT && with_da) off = round_up(off + sizeof(float) * y.nchunks * B * G * D);
+  y.state = off;
+  if (op == PARARNN_OP_SOLVE && K >= 2) off = round_up(off + sizeof(float) * NS * B * L * D);
+  y.total = off;
+  return y;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// widest channel group C in {4, 2, 1} (at most cmax) that divides D and keeps
+// every pointer aligned
+int pick_c(int cmax, int D, size_t usize, const void* u, std::initializer_list<const void*> f32ptrs) {
+  for (int C : {4, 2, 1}) {
+    if (C > cmax || D % C) continue;
+    bool ok = aligned(u, usize * C);
+    for (const void* q : f32ptrs)
+      if (q && !aligned(q, sizeof(float) * C)) ok = false;
+    if (ok) return C;
+  }
+  return 0;
+}
+
+int check_hip(hipError_t e) { return e == hipSuccess ? PARARNN_OK : PARARNN_EHIP; }
+
+int record(const pararnn_opts* o, int i, hipStream_t s) {
+  if (!o->events || !o->events[i]) return PARARNN_OK;
+  return check_hip(hipEventRecord(static_cast<hipEvent_t>(o->events[i]), s));
+}
+
+int clear_ws(char* ws, const Layout& y, float* user, long long nuser, hipStream_t s) {
+  const long long n16 = static_cast<long long>(y.zero_end / 16);
+  const long long work = n16 > nuser ? n16 : nuser;
+  long long blocks = (work + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(ws_clear_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                     reinterpret_cast<f32x4*>(ws), n16, user, nuser);
+  return check_hip(hipGetLastError());
+}
+
+template <class Cell, class UT, int C>
+int launch_iter(const IterArgs& a, hipStream_t s) {
+  using K = Cfg<Cell, C, false>;
+  constexpr int CW = (64 / K::LL) * C;
+  const unsigned ntiles_d = static_cast<unsigned>((a.D + CW - 1) / CW);
+  const unsigned grid = static_cast<unsigned>(a.B) * ntiles_d * static_cast<unsigned>(a.nchunks);
+  IterArgs b = a;
+  b.ntiles_d = static_cast<int>(ntiles_d);
+  hipLaunchKernelGGL((newton_iter_kernel<Cell, UT, C, K::T, K::W, K::LL>), dim3(grid), dim3(64 * K::W), 0,
+                     s, b);
+  return check_hip(hipGetLastError());
+}
+
+template <class Cell, class UT>
+int launch_iter_c(int C, const IterArgs& a, hipStream_t s) {
+  switch (C) {
+    case 4: return launch_iter<Cell, UT, 4>(a, s);
+    case 2: return launch_iter<Cell, UT, 2>(a, s);
+    default: return launch_iter<Cell, UT, 1>(a, s);
+  }
+}
+
+template <class Cell>
+int launch_iter_any(int dtype, int C, const IterArgs& a, hipStream_t s) {
+  if constexpr (Cell::NS == 2) C = C > 2 ? 2 : C;
+  return dtype == PARARNN_BF16 ? launch_iter_c<Cell, bf16>(C, a, s) : launch_iter_c<Cell, float>(C, a, s);
+}
+
+template <class Cell, class UT, int C>
+int launch_adj(const AdjArgs& a, hipStream_t s) {
+  using K = Cfg<Cell, C, true>;
+  constexpr int CW = (64 / K::LL) * C;
+  const unsigned ntiles_d = static_cast<unsigned>((a.D + CW - 1) / CW);
+  const unsigned grid = static_cast<unsigned>(a.B) * ntiles_d * static_cast<unsigned>(a.nchunks);
+  AdjArgs b = a;
+  b.ntiles_d = static_cast<int>(ntiles_d);
+  hipLaunchKernelGGL((adjoint_kernel<Cell, UT, C, K::T, K::W, K::LL>), dim3(grid), dim3(64 * K::W), 0, s, b);
+  return check_hip(hipGetLastError());
+}
+
+template <class Cell, class UT>
+int launch_adj_c(int C, const AdjArgs& a, hipStream_t s) {
+  switch (C) {
+    case 4: return launch_adj<Cell, UT, 4>(a, s);
+    case 2: return launch_adj<Cell, UT, 2>(a, s);
+    default: return launch_adj<Cell, UT, 1>(a, s);
+  }
+}
+
+template <class Cell>
+int launch_adj_any(int dtype, int C, const AdjArgs& a, hipStream_t s) {
+  return dtype == PARARNN_BF16 ? launch_adj_c<Cell, bf16>(C, a, s) : launch_adj_c<Cell, float>(C, a, s);
+}
+
+int solve(int cell, const void* u, const float* a, const float* c0, const float* h0, float* c, float* h,
+          void* ws, size_t ws_bytes, const pararnn_opts* o, int32_t* iters, int32_t* converged,
+          float* max_update, hipStream_t stream) {
+  if (!opts_ok(cell, PARARNN_OP_SOLVE, o)) return PARARNN_EINVAL;
+  if (!u || !a || !h || !ws || (cell == PARARNN_LSTM && !c)) return PARARNN_EINVAL;
+  if (o->u_dtype != PARARNN_F32 && o->u_dtype != PARARNN_BF16) return PARARNN_EUNSUPPORTED;
+  if (o->early_exit != 0 && o->early_exit != 1) return PARARNN_EINVAL;
+  const Layout y = layout(cell, PARARNN_OP_SOLVE, o, false);
+  if (ws_bytes < y.total) return PARARNN_EWORKSPACE;
+  if (!aligned(ws, kAlign)) return PARARNN_EUNSUPPORTED;
+  const size_t usize = o->u_dtype == PARARNN_BF16 ? 2 : 4;
+  const int C = pick_c(cell == PARARNN_LSTM ? 2 : 4, o->D, usize, u, {a, h0, h, c0, c});
+  if (!C || !aligned(u, usize)) return PARARNN_EUNSUPPORTED;
+
+  const int K = o->max_iters, NS = nstate(cell);
+  const size_t BLD = static_cast<size_t>(o->B) * o->L * o->D;
+  char* w = static_cast<char*>(ws);
+  float* buf = reinterpret_cast<float*>(w + y.state);
+  float* out[2] = {cell == PARARNN_LSTM ? c : h, cell == PARARNN_LSTM ? h : nullptr};
+  float* alt[2] = {buf, NS == 2 ? buf + BLD : nullptr};
+
+  int rc = record(o, 0, stream);
+  if (rc) return rc;
+  rc = clear_ws(w, y, max_update, max_update ? static_cast<long long>(K) * o->B : 0, stream);
+  if (rc) return rc;
+  rc = record(o, 1, stream);
+  if (rc) return rc;
+
+  IterArgs ia;
+  memset(&ia, 0, sizeof(ia));
+  ia.u = u;
+  ia.a = a;
+  ia.s0[0] = cell == PARARNN_LSTM ? c0 : h0;
+  ia.s0[1] = cell == PARARNN_LSTM ? h0 : nullptr;
+  ia.incl = reinterpret_cast<unsigned long long*>(w + y.incl);
+  ia.agg = reinterpret_cast<unsigned long long*>(w + y.agg);
+  ia.ctr = reinterpret_cast<unsigned int*>(w + y.ctr);
+  ia.maxupd = reinterpret_cast<unsigned int*>(w + y.maxupd);
+  ia.iters_out = iters;
+  ia.conv_out = converged;
+  ia.maxupd_out = max_update;
+  ia.B = o->B;
+  ia.L = o->L;
+  ia.D = o->D;
+  ia.K = K;
+  ia.nchunks = y.nchunks;
+  ia.early_exit = o->early_exit;
+  ia.tol = o->tol;
+  // ping-pong so that iterate K lands in the caller's output
+  for (int k = 1; k <= K; ++k) {
+    const bool k_in_out = ((K - k) % 2) == 0;
+    for (int s = 0; s < NS; ++s) {
+      ia.sout[s] = k_in_out ? out[s] : alt[s];
+      ia.sin[s] = (k == 1) ? nullptr : (k_in_out ? alt[s] : out[s]);
+    }
+    ia.k = k;
+    rc = (cell == PARARNN_LSTM) ? launch_iter_any<LstmCell>(o->u_dtype, C, ia, stream)
+                                : launch_iter_any<GruCell>(o->u_dtype, C, ia, stream);
+    if (rc) return rc;
+    rc = record(o, k + 1, stream);
+    if (rc) return rc;
+  }
+  return PARARNN_OK;
+}
+
+}  // namespace
+}  // namespace pararnn
+
+using namespace pararnn;
+
+extern "C" size_t pararnn_workspace_bytes(int32_t cell, int32_t op, const pararnn_opts* o) {
+  if (!opts_ok(cell, op, o)) return 0;
+  return layout(cell, op, o, true).total;
+}
+
+extern "C" int32_t pararnn_solve_gru(const void* u, const float* a, const float* h0, float* h, void* ws,
+                                     size_t ws_bytes, const pararnn_opts* o, int32_t* iters,
+                                     int32_t* converged, float* max_update, void* stream) {
+  return solve(PARARNN_GRU, u, a, nullptr, h0, nullptr, h, ws, ws_bytes, o, iters, converged, max_update,
+               static_cast<hipStream_t>(stream));
+}
+
+extern "C" int32_t pararnn_solve_lstm(const void* u, const float* a, const float* c0, const float* h0,
+                                      float* c, float* h, void* ws, size_t ws_bytes, const pararnn_opts* o,
+                                      int32_t* iters, int32_t* converged, float* max_update, void* stream) {
+  return solve(PARARNN_LSTM, u, a, c0, h0, c, h, ws, ws_bytes, o, iters, converged, max_update,
+               static_cast<hipStream_t>(stream));
+}
+
+extern "C" int32_t pararnn_adjoint(int32_t cell, const void* u, const float* a, const float* c0,
+                                   const float* h0, const float* c, const float* h, const float* dh,
+                                   float* du, float* ds0, float* da, void* ws, size_t ws_bytes,
+                                   const pararnn_opts* o, void* stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if (!opts_ok(cell, PARARNN_OP_ADJOINT, o)) return PARARNN_EINVAL;
+  if (!u || !a || !h || !dh || !du || !ws || (cell == PARARNN_LSTM && !c)) return PARARNN_EINVAL;
+  if (o->u_dtype != PARARNN_F32 && o->u_dtype != PARARNN_BF16) return PARARNN_EUNSUPPORTED;
+  const Layout y = layout(cell, PARARNN_OP_ADJOINT, o, da != nullptr);
+  if (ws_bytes < y.total) return PARARNN_EWORKSPACE;
+  if (!aligned(ws, kAlign)) return PARARNN_EUNSUPPORTED;
+  const size_t usize = o->u_dtype == PARARNN_BF16 ? 2 : 4;
+  const bool lstm = cell == PARARNN_LSTM;
+  const int C = pick_c(lstm ? 2 : 4, o->D, usize, u,
+                      {a, h0, h, dh, du, ds0, da, lstm ? c0 : nullptr, lstm ? c : nullptr});
+  if (!C || !aligned(u, usize)) return PARARNN_EUNSUPPORTED;
+  char* w = static_cast<char*>(ws);
+
+  int rc = record(o, 0, stream);
+  if (rc) return rc;
+  rc = clear_ws(w, y, nullptr, 0, stream);
+  if (rc) return rc;
+  rc = record(o, 1, stream);
+  if (rc) return rc;
+
+  AdjArgs aa;
+  memset(&aa, 0, sizeof(aa));
+  aa.u = u;
+  aa.a = a;
+  aa.s0[0] = lstm ? c0 : h0;
+  aa.s0[1] = lstm ? h0 : nullptr;
+  aa.S[0] = lstm ? c : h;
+  aa.S[1] = lstm ? h : nullptr;
+  aa.dh = dh;
+  aa.du = du;
+  aa.ds0 = ds0;
+  aa.da_part = da ? reinterpret_cast<float*>(w + y.dapart) : nullptr;
+  aa.incl = reinterpret_cast<unsigned long long*>(w + y.incl);
+  aa.agg = reinterpret_cast<unsigned long long*>(w + y.agg);
+  aa.ctr = reinterpret_cast<unsigned int*>(w + y.ctr);
+  aa.B = o->B;
+  aa.L = o->L;
+  aa.D = o->D;
+  aa.nchunks = y.nchunks;
+  rc = lstm ? launch_adj_any<LstmCell>(o->u_dtype, C, aa, stream)
+            : launch_adj_any<GruCell>(o->u_dtype, C, aa, stream);
+  if (rc) return rc;
+  if (da) {
+    const int G = ngates(cell);
+    const long long n = static_cast<long long>(G) * o->D;
+    hipLaunchKernelGGL(da_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream,
+                       reinterpret_cast<const float*>(w + y.dapart), da, y.nchunks, o->B, G, o->D);
+    rc = check_hip(hipGetLastError());
+    if (rc) return rc;
+  }
+  return record(o, 2, stream);
+}
+
+extern "C" const char* pararnn_strerror(int32_t status) {
+  switch (status) {
+    case PARARNN_OK: return "ok";
+    case PARARNN_EINVAL: return "invalid argument (null pointer, non-positive size, bad enum or iteration count, size overflow)";
+    case PARARNN_EUNSUPPORTED: return "unsupported dtype or misaligned pointer";
+    case PARARNN_EWORKSPACE: return "workspace smaller than pararnn_workspace_bytes()";
+    case PARARNN_EHIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}

@@ -1,0 +1,99 @@
+"""C-ABI contract checks that need no GPU: the library loads, exports every
+function include/pararnn.h declares, sizes its workspace, and rejects invalid
+arguments with the documented status before launching anything."""
+import ctypes
+import re
+
+import pytest
+
+from nonlinear_rnn_solve_newton_amd import binding as b
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not b.LIB_PATH.exists():
+        from nonlinear_rnn_solve_newton_amd import build
+        build.build()
+    return b.lib()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = b.header_functions()
+    assert set(names) == {"pararnn_workspace_bytes", "pararnn_solve_gru", "pararnn_solve_lstm",
+                          "pararnn_adjoint", "pararnn_strerror"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_codes_match_header(lib):
+    text = b.HEADER.read_text()
+    codes = dict((m[0], int(m[1])) for m in re.findall(r"#define (PARARNN_E?[A-Z]+) \((-?\d+)\)", text))
+    codes["PARARNN_OK"] = int(re.search(r"#define PARARNN_OK (\d+)", text).group(1))
+    assert codes == {"PARARNN_OK": 0, "PARARNN_EINVAL": -1, "PARARNN_EUNSUPPORTED": -2,
+                     "PARARNN_EWORKSPACE": -3, "PARARNN_EHIP": -4}
+    for v in codes.values():
+        assert b.strerror(v) != "unknown status"
+    assert b.strerror(7) == "unknown status"
+
+
+def test_opts_struct_layout():
+    assert ctypes.sizeof(b.Opts) == 40
+    assert b.Opts.events.offset == 32
+
+
+def test_workspace_bytes(lib):
+    # solve: counters, row maxima, descriptors, one ping-pong state buffer (K >= 2)
+    B, L, D = 8, 4096, 1024
+    n = b.workspace_bytes("gru", b.OP_SOLVE, B, L, D, 3)
+    assert n >= 4 * B * L * D
+    assert b.workspace_bytes("lstm", b.OP_SOLVE, B, L, D, 3) >= 8 * B * L * D
+    # K = 1 needs no state buffer
+    assert b.workspace_bytes("gru", b.OP_SOLVE, B, L, D, 1) < 4 * B * L * D
+    # single chunk: no descriptors
+    assert b.workspace_bytes("gru", b.OP_SOLVE, 1, 100, 64, 1) <= 4096
+    # invalid options -> 0
+    assert b.workspace_bytes("gru", b.OP_SOLVE, 0, L, D, 3) == 0
+    assert b.workspace_bytes("gru", b.OP_SOLVE, B, L, D, 0) == 0
+    o, _ = b.make_opts(B, L, D, 3)
+    assert lib.pararnn_workspace_bytes(7, 0, ctypes.byref(o)) == 0
+    assert lib.pararnn_workspace_bytes(0, 5, ctypes.byref(o)) == 0
+    assert lib.pararnn_workspace_bytes(0, 0, None) == 0
+
+
+def _solve_status(lib, u=1, a=1, h=1, ws=1, ws_bytes=1 << 40, B=2, L=8, D=4, K=3, dtype=1, early=0):
+    o, _ = b.make_opts(B, L, D, K, 1e-4, early, dtype)
+    o.early_exit = early
+    P = lambda v: ctypes.c_void_p(v * 4096) if v else None  # noqa: E731  (never dereferenced)
+    return lib.pararnn_solve_gru(P(u), P(a), None, P(h), P(ws), ws_bytes, ctypes.byref(o), None, None,
+                                 None, None)
+
+
+def test_invalid_arguments_rejected_before_launch(lib):
+    assert _solve_status(lib, u=0) == b.__dict__.get("EINVAL", -1)
+    assert _solve_status(lib, a=0) == -1
+    assert _solve_status(lib, h=0) == -1
+    assert _solve_status(lib, ws=0) == -1
+    assert _solve_status(lib, B=0) == -1
+    assert _solve_status(lib, L=-3) == -1
+    assert _solve_status(lib, D=0) == -1
+    assert _solve_status(lib, K=0) == -1
+    assert _solve_status(lib, early=2) == -1
+    assert _solve_status(lib, dtype=5) == -2
+    assert _solve_status(lib, ws_bytes=16) == -3
+    o, _ = b.make_opts(2, 8, 4, 3)
+    assert lib.pararnn_solve_gru(None, None, None, None, None, 0, None, None, None, None, None) == -1
+    assert lib.pararnn_solve_lstm(ctypes.c_void_p(4096), ctypes.c_void_p(4096), None, None, None,
+                                  ctypes.c_void_p(4096), ctypes.c_void_p(4096), 1 << 40, ctypes.byref(o),
+                                  None, None, None, None) == -1  # c missing
+    assert lib.pararnn_adjoint(0, None, None, None, None, None, None, None, None, None, None, None, 0,
+                               ctypes.byref(o), None) == -1
+    assert lib.pararnn_adjoint(3, ctypes.c_void_p(4096), ctypes.c_void_p(4096), None, None, None,
+                               ctypes.c_void_p(4096), ctypes.c_void_p(4096), ctypes.c_void_p(4096), None,
+                               None, ctypes.c_void_p(4096), 1 << 40, ctypes.byref(o), None) == -1
+
+
+def test_misaligned_workspace_rejected(lib):
+    o, _ = b.make_opts(2, 8, 4, 3)
+    st = lib.pararnn_solve_gru(ctypes.c_void_p(4096), ctypes.c_void_p(4096), None, ctypes.c_void_p(4096),
+                               ctypes.c_void_p(4096 + 16), 1 << 40, ctypes.byref(o), None, None, None, None)
+    assert st == -2

@@ -1,0 +1,158 @@
+"""GPU parity of the Newton solve (HIP path through the C ABI) against the fp64
+oracle, on the same seeded inputs: states within 1e-4 (max-abs), iteration
+count and convergence flags bit-exact where the oracle's update size is clear
+of the tolerance."""
+import numpy as np
+import pytest
+import torch
+
+from nonlinear_rnn_solve_newton_amd import binding
+from nonlinear_rnn_solve_newton_amd.workloads import make_inputs
+from oracle import oracle as O
+from tests.helpers import (STATE_TOL, assert_close, check_flags, gpu_solve, s0_float32, say)
+
+pytestmark = pytest.mark.gpu
+
+# (B, L, D): single step, tiny, one lane, odd D (C = 1), D % 4 == 2 (C = 2), ragged
+# channel tiles, ragged chunks, many chunks
+SHAPES = [
+    (1, 1, 1), (1, 2, 3), (2, 3, 2), (3, 5, 64), (1, 63, 65), (2, 64, 6), (1, 65, 4),
+    (1, 127, 1000), (2, 128, 66), (1, 129, 128), (3, 1000, 64), (2, 1000, 200),
+    (1, 4097, 3), (1, 5000, 130), (2, 300, 1000),
+]
+
+
+@pytest.mark.parametrize("cell", ["gru", "lstm"])
+@pytest.mark.parametrize("u_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("B,L,D", SHAPES, ids=[f"{b}x{l}x{d}" for b, l, d in SHAPES])
+def test_solve_matches_oracle(cell, u_dtype, B, L, D):
+    say(f"solve {cell} {u_dtype} B={B} L={L} D={D}")
+    x = make_inputs(cell, B, L, D, seed=1000 + B * 7 + L * 3 + D, u_dtype=u_dtype)
+    S, iters, conv, mu = gpu_solve(cell, x, iters=3)
+    want, upd = O.newton(cell, x.u, x.a, K=3)
+    assert_close(S, want, STATE_TOL, f"{cell} state")
+    assert_close(mu, upd, 1e-4, "max_update")
+    check_flags(iters, conv, upd, 3, 1e-4)
+
+
+@pytest.mark.parametrize("cell", ["gru", "lstm"])
+@pytest.mark.parametrize("K", [1, 2, 4])
+def test_iteration_counts(cell, K):
+    say(f"solve {cell} K={K}")
+    x = make_inputs(cell, 2, 700, 96, seed=77 + K, u_dtype="bf16")
+    S, iters, conv, mu = gpu_solve(cell, x, iters=K)
+    want, upd = O.newton(cell, x.u, x.a, K=K)
+    assert_close(S, want, STATE_TOL, f"{cell} K={K}")
+    check_flags(iters, conv, upd, K, 1e-4)
+
+
+@pytest.mark.parametrize("cell", ["gru", "lstm"])
+def test_initial_state(cell):
+    say(f"solve {cell} with initial state")
+    B, L, D = 3, 400, 68
+    x = make_inputs(cell, B, L, D, seed=5, u_dtype="bf16")
+    NS = 2 if cell == "lstm" else 1
+    s0 = np.random.default_rng(0).normal(size=(NS, B, D)).astype(np.float32)
+    S, iters, conv, mu = gpu_solve(cell, x, iters=3, s0=s0)
+    want, upd = O.newton(cell, x.u, x.a, K=3, s0=s0_float32(s0))
+    assert_close(S, want, STATE_TOL, f"{cell} with s0")
+
+
+@pytest.mark.parametrize("cell", ["gru", "lstm"])
+def test_finite_termination_rows(cell):
+    """After K iterations the first K rows equal the sequential trajectory."""
+    say(f"solve {cell} finite termination")
+    x = make_inputs(cell, 2, 3000, 64, seed=9, u_dtype="bf16")
+    S, *_ = gpu_solve(cell, x, iters=3)
+    seq = O.seq(cell, x.u, x.a)
+    assert_close(S[:, :, :3], seq[:, :, :3], 1e-5, "rows l < K")
+
+
+def test_gru_linear_cell_converges_in_one_step():
+    say("solve gru a=0")
+    x = make_inputs("gru", 2, 2000, 128, seed=3, u_dtype="bf16", a_zero=True)
+    S, iters, conv, mu = gpu_solve("gru", x, iters=2)
+    seq = O.seq("gru", x.u, x.a)
+    assert_close(S, seq, 1e-5, "a=0 GRU vs sequential")
+    assert mu[1].max() < 1e-6 and list(conv) == [1, 1] and iters == 2
+
+
+@pytest.mark.parametrize("cell,K,amax", [("gru", 6, 1.0), ("lstm", 8, 1.0), ("gru", 5, 0.3)])
+def test_convergence_flags_true_branch(cell, K, amax):
+    say(f"solve {cell} K={K} amax={amax} converging")
+    x = make_inputs(cell, 2, 512, 64, seed=13, u_dtype="bf16", amax=amax)
+    S, iters, conv, mu = gpu_solve(cell, x, iters=K)
+    want, upd = O.newton(cell, x.u, x.a, K=K)
+    assert_close(S, want, STATE_TOL, "state")
+    check_flags(iters, conv, upd, K, 1e-4)
+    assert conv.all(), f"expected convergence after {K} iterations, oracle updates {upd[-1]}"
+
+
+@pytest.mark.parametrize("cell,K", [("gru", 8), ("lstm", 10)])
+def test_early_exit(cell, K):
+    say(f"solve {cell} early exit K={K}")
+    x = make_inputs(cell, 3, 600, 64, seed=17, u_dtype="bf16")
+    S, iters, conv, mu = gpu_solve(cell, x, iters=K, early_exit=True)
+    want_full, upd = O.newton(cell, x.u, x.a, K=K)
+    want_iters, want_conv = O.flags(upd, 1e-4, early_exit=True)
+    amb = check_flags(iters, conv, upd, K, 1e-4, early_exit=True)
+    assert amb == 0, "ambiguous case; pick another seed"
+    assert iters == want_iters < K
+    want, _ = O.newton(cell, x.u, x.a, K=iters)
+    assert_close(S, want, STATE_TOL, "state at the stopping iteration")
+    assert np.all(mu[iters:] == 0.0)
+
+
+def test_nan_input_propagates():
+    say("solve gru NaN input")
+    x = make_inputs("gru", 3, 500, 64, seed=23, u_dtype="f32")
+    u = x.u.clone()
+    u[1, 200, 0, 5] = float("nan")
+    S, iters, conv, mu = gpu_solve("gru", x, iters=3, u=u)
+    assert np.isnan(mu[:, 1]).all() and np.isfinite(mu[:, [0, 2]]).all()
+    assert conv[1] == 0
+    assert np.isnan(S[0, 1, 200:, 5]).all()
+    want, _ = O.newton("gru", x.u, x.a, K=3)
+    ok = [0, 2]
+    assert_close(S[:, ok], want[:, ok], STATE_TOL, "rows without NaN")
+
+
+@pytest.mark.parametrize("cell", ["gru", "lstm"])
+def test_deterministic_and_workspace_reuse(cell):
+    say(f"solve {cell} determinism")
+    x = make_inputs(cell, 2, 3000, 256, seed=29, u_dtype="bf16")
+    d = torch.device("cuda:0")
+    u, a = x.u.to(d), x.a.to(d)
+    r1 = binding.solve(cell, u, a)
+    h1 = r1["h"].clone()
+    r2 = binding.solve(cell, u, a, ws=r1["ws"])
+    torch.cuda.synchronize()
+    assert torch.equal(h1, r2["h"])
+    if cell == "lstm":
+        assert torch.equal(r1["c"], r2["c"])
+
+
+@pytest.mark.parametrize("cell", ["gru", "lstm"])
+def test_misaligned_pointers_use_narrow_path(cell):
+    """u and a at a 4-byte (not 16-byte) offset select the one-channel path."""
+    say(f"solve {cell} misaligned")
+    B, L, D = 2, 300, 64
+    x = make_inputs(cell, B, L, D, seed=31, u_dtype="f32")
+    d = torch.device("cuda:0")
+    ubuf = torch.empty(x.u.numel() + 1, dtype=torch.float32, device=d)
+    u = ubuf[1:].view(x.u.shape)
+    u.copy_(x.u.to(d))
+    r = binding.solve(cell, u, x.a.to(d))
+    torch.cuda.synchronize()
+    want, _ = O.newton(cell, x.u, x.a, K=3)
+    S = np.stack([t.cpu().double().numpy() for t in ([r["h"]] if cell == "gru" else [r["c"], r["h"]])])
+    assert_close(S, want, STATE_TOL, "misaligned")
+
+
+def test_invalid_arguments_raise():
+    d = torch.device("cuda:0")
+    u = torch.zeros(1, 4, 3, 8, device=d)
+    with pytest.raises(binding.PararnnError):
+        binding.solve("gru", u, torch.zeros(3, 8, device=d), iters=0)
+    with pytest.raises(binding.PararnnError):
+        binding.solve("gru", u.half(), torch.zeros(3, 8, device=d))
