@@ -1,0 +1,272 @@
+"""Throughput of the 3-Newton ParaGRU / ParaLSTM solve on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one whole solve (workspace reset + K fused Newton-iteration
+launches; for the adjoint workload also the reverse-scan launch) over one
+batch of seeded synthetic inputs already resident in HBM. Prints one JSON line
+with the throughput in solved state elements (B*L*D) per second, the HBM
+roofline fraction of the Newton-iteration kernel (algorithmic bytes per launch
+over its mean duration, measured with HIP events recorded around every launch
+on the stream the kernels run on) and the fp64 CPU oracle timed on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak
+
+# algorithmic HBM bytes per state element for one Newton-iteration launch:
+# read the gate inputs (G per element) and, after the first iteration, the
+# previous iterate; write the new iterate (NS fp32 state components).
+def iter_bytes(cell: str, u_bytes: int, k: int) -> int:
+    G, NS = (3, 1) if cell == "gru" else (4, 2)
+    return G * u_bytes + NS * 4 * (1 if k == 1 else 2)
+
+
+# adjoint: read u, the trajectory and dh, write du (fp32)
+def adjoint_bytes(cell: str, u_bytes: int) -> int:
+    G, NS = (3, 1) if cell == "gru" else (4, 2)
+    return G * u_bytes + NS * 4 + 4 + G * 4
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for p in sorted((ROOT / "nonlinear_rnn_solve_newton_amd" / "csrc").glob("*")):
+        h.update(p.read_bytes())
+    return h.hexdigest()[:16]
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime's C API."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        evs = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            evs.append(e.value)
+        return evs
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        if self.hip.hipEventSynchronize(ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+        if self.hip.hipEventElapsedTime(ctypes.byref(out), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(out.value)
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def load_traffic(workload: str, digest: str):
+    """Counter-measured HBM bytes per launch for the current kernel sources, if profiled."""
+    f = ROOT / "profiles" / f"newton_iter_{workload}_traffic.json"
+    if not f.exists():
+        return None
+    try:
+        d = json.loads(f.read_text())
+    except ValueError:
+        return None
+    if d.get("source_digest") != digest:
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(w, x, iters, target_s=12.0):
+    """fp64 oracle Newton solve on a channel sample of the same workload."""
+    from nonlinear_rnn_solve_newton_amd.workloads import gather_channels, sample_channels
+    from oracle import oracle as O
+
+    nthreads = O.default_threads()
+    BD = w.B * w.D
+
+    def run(n):
+        ch = sample_channels(w.B, w.D, n, seed=99)
+        u = gather_channels(x.u, ch, w.D)
+        a = x.a[:, ch % w.D].contiguous()
+        t0 = time.perf_counter()
+        O.newton(w.cell, u, a, K=iters, nthreads=nthreads)
+        t1 = time.perf_counter()
+        O.seq(w.cell, u, a, nthreads=nthreads)
+        t2 = time.perf_counter()
+        return len(ch), t1 - t0, t2 - t1
+
+    n0 = min(BD, max(nthreads, 16))
+    n, t_newton, _ = run(n0)
+    per_chan = t_newton / n
+    n = int(min(BD, max(n0, target_s / max(per_chan, 1e-9))))
+    n = max(nthreads, n - n % max(nthreads, 1)) if n < BD else n
+    n, t_newton, t_seq = run(n)
+    elems = n * w.L
+    return {
+        "value": elems / t_newton,
+        "unit": "elems/s",
+        "cores": nthreads,
+        "kind": "oracle",
+        "sample": f"{n} of {BD} channels (b, d) over the full L={w.L}, {iters} fp64 Newton iterations; "
+                  f"{t_newton:.2f} s",
+        "sequential_value": elems / t_seq,
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration for profiling)")
+    args = ap.parse_args(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; the multi-GPU sharding is a design "
+                                   "note, not an implementation", "n_gpus": args.gpus}))
+        return 2
+
+    import torch
+
+    sys.path.insert(0, str(ROOT))
+    from nonlinear_rnn_solve_newton_amd import binding
+    from nonlinear_rnn_solve_newton_amd.workloads import HEADLINE, WORKLOADS, workload_inputs
+
+    w = WORKLOADS[args.workload or HEADLINE]
+    K = w.iters
+    dev = torch.device("cuda:0")
+    x = workload_inputs(w)
+    u, a = x.u.to(dev), x.a.to(dev)
+    dh = x.dh.to(dev) if w.adjoint else None
+    u_bytes = 2 if w.u_dtype == "bf16" else 4
+    torch.cuda.synchronize()
+
+    hip = HipEvents()
+    ev = hip.create(K + 2)
+    ev_adj = hip.create(3) if w.adjoint else None
+    first = binding.solve(w.cell, u, a, iters=K)
+    ws, out = first["ws"], {k: first[k] for k in ("h", "c") if k in first}
+    gadj = binding.adjoint(w.cell, u, a, out["h"], dh, c=out.get("c")) if w.adjoint else None
+
+    def step(events=None, events_adj=None):
+        r = binding.solve(w.cell, u, a, iters=K, ws=ws, out=out, events=events)
+        if w.adjoint:
+            binding.adjoint(w.cell, u, a, out["h"], dh, c=out.get("c"), ws=gadj["ws"], du=gadj["du"],
+                            events=events_adj)
+        return r
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    launch_ms = [[] for _ in range(K)]
+    clear_ms, adj_ms = [], []
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step(ev, ev_adj)
+        # per-launch times: read back after the step (events are reused)
+        clear_ms.append(hip.ms(ev[0], ev[1]))
+        for k in range(K):
+            launch_ms[k].append(hip.ms(ev[k + 1], ev[k + 2]))
+        if w.adjoint:
+            adj_ms.append(hip.ms(ev_adj[1], ev_adj[2]))
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / args.steps
+
+    # the event read-backs synchronise once per step; time again without them
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    ms_step_free = start.elapsed_time(stop) / args.steps
+
+    N = w.N
+    mean = lambda v: sum(v) / len(v)  # noqa: E731
+    iter_ms = [mean(v) for v in launch_ms]
+    bytes_k = [iter_bytes(w.cell, u_bytes, k + 1) * N for k in range(K)]
+    achieved = sum(bytes_k) / K / (mean(iter_ms) * 1e-3) / 1e9
+    digest = source_digest()
+    traffic = load_traffic(w.name, digest)
+    result = {
+        "metric": "solved state elems/s (B*L*D) per 3-Newton solve; HBM GB/s as % of peak",
+        "value": N / (ms_step_free * 1e-3),
+        "unit": "elems/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step_free,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; u ~ N(0,1) stored " + w.u_dtype + ", a ~ U(-amax, amax))",
+        "config": {"workload": w.name, "cell": w.cell, "B": w.B, "L": w.L, "D": w.D,
+                   "newton_iters": K, "u_dtype": w.u_dtype, "adjoint": w.adjoint},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "newton_iter_kernel",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": bytes_k,
+            "launch_ms": iter_ms,
+        },
+        "timing": {
+            "ms_per_step_with_event_readback": ms_step,
+            "workspace_clear_ms": mean(clear_ms),
+            "newton_iter_ms": iter_ms,
+            "source_digest": digest,
+        },
+    }
+    if w.adjoint:
+        amean = mean(adj_ms)
+        result["timing"]["adjoint_ms"] = amean
+        result["adjoint_roofline"] = {
+            "bound": "hbm", "kernel": "adjoint_kernel",
+            "achieved": adjoint_bytes(w.cell, u_bytes) * N / (amean * 1e-3) / 1e9,
+            "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": adjoint_bytes(w.cell, u_bytes) * N / (amean * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        }
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = src.numel() * 4
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, x, K)
+    hip.destroy(ev + (ev_adj or []))
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -24,7 +24,9 @@ struct bf16 {
 __device__ __forceinline__ float sigm(float x) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.4426950408889634f));
 }
-__device__ __forceinline__ float tanh_fast(float x) { return fmaf(2.0f, sigm(2.0f * x), -1.0f); }
+__device__ __forceinline__ float tanh_fast(float x) {
+  return fmaf(2.0f, __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -2.8853900817779268f)), -1.0f);
+}
 
 // ---------------------------------------------------------------------------
 // vector loads / stores of C consecutive channels (C in {1, 2, 4}); the host
@@ -39,6 +41,21 @@ __device__ __forceinline__ void ld_f32(const float* p, float (&v)[C]) {
     v[0] = x.x; v[1] = x.y;
   } else {
     v[0] = *p;
+  }
+}
+
+// Streaming loads (read once per launch): nontemporal, so they do not displace
+// reusable lines in the caches.
+template <int C>
+__device__ __forceinline__ void ld_f32_stream(const float* p, float (&v)[C]) {
+  if constexpr (C == 4) {
+    const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  } else if constexpr (C == 2) {
+    const f32x2 x = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(p));
+    v[0] = x.x; v[1] = x.y;
+  } else {
+    v[0] = __builtin_nontemporal_load(p);
   }
 }
 
@@ -65,7 +82,7 @@ struct URaw;
 template <int C>
 struct URaw<float, C> {
   float v[C];
-  __device__ __forceinline__ void load(const float* p) { ld_f32<C>(p, v); }
+  __device__ __forceinline__ void load(const float* p) { ld_f32_stream<C>(p, v); }
   __device__ __forceinline__ void zero() {
 #pragma unroll
     for (int c = 0; c < C; ++c) v[c] = 0.0f;
@@ -79,13 +96,13 @@ struct URaw<bf16, C> {
   uint32_t w[NW];
   __device__ __forceinline__ void load(const bf16* p) {
     if constexpr (C == 4) {
-      const u32x2 x = *reinterpret_cast<const u32x2*>(p);
+      const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
       w[0] = x.x;
       w[1] = x.y;
     } else if constexpr (C == 2) {
-      w[0] = *reinterpret_cast<const uint32_t*>(p);
+      w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
     } else {
-      w[0] = static_cast<uint32_t>(p->bits);
+      w[0] = static_cast<uint32_t>(__builtin_nontemporal_load(&p->bits));
     }
   }
   __device__ __forceinline__ void zero() {
@@ -264,6 +281,34 @@ struct Aff {
       }
     }
     *this = r;
+  }
+
+  // this <- (J, r) o this, in place: A = J A, b = J b + r
+  __device__ __forceinline__ void pre(const float (&J)[NS][NS][C], const float (&r)[NS][C]) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      float nA[NS][NS], nb[NS];
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+          float a2 = J[i][0][c] * A[0][j][c];
+#pragma unroll
+          for (int k = 1; k < NS; ++k) a2 = fmaf(J[i][k][c], A[k][j][c], a2);
+          nA[i][j] = a2;
+        }
+        float b2 = r[i][c];
+#pragma unroll
+        for (int k = 0; k < NS; ++k) b2 = fmaf(J[i][k][c], b[k][c], b2);
+        nb[i] = b2;
+      }
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+#pragma unroll
+        for (int j = 0; j < NS; ++j) A[i][j][c] = nA[i][j];
+        b[i][c] = nb[i];
+      }
+    }
   }
 
   // y = A x + b on vectors x[NS][C]

@@ -34,11 +34,9 @@ struct IterArgs {
   float* sout[2];         // iterate k per component
   unsigned long long* incl;  // [nchunks][NS][B*D] inclusive carries (value at chunk end)
   unsigned long long* agg;   // [nchunks][NS*NS+NS][B*D] chunk transforms
-  unsigned int* ctr;      // [0,K) tickets, [K,2K) finished-workgroup counts, [2K] stop flag
-  unsigned int* maxupd;   // [K][B] fp32 bits of max |update|
-  int32_t* iters_out;     // [1] or nullptr
-  int32_t* conv_out;      // [B] or nullptr
-  float* maxupd_out;      // [K][B] or nullptr
+  unsigned int* ctr;      // [0,K) tickets
+  unsigned int* maxupd;   // [K][B] fp32 bits of max |update| (reduced from pmax)
+  unsigned int* pmax;     // [K][grid] per-workgroup max |update| bits, indexed by ticket
   int B, L, D, k, K, nchunks, ntiles_d, early_exit;
   float tol;
 };
@@ -140,21 +138,26 @@ __global__ void __launch_bounds__(64 * W) newton_iter_kernel(const IterArgs p) {
 
   __shared__ float s_agg[W][NA][CW];
   __shared__ float s_carry[NS][CW];
-  __shared__ unsigned int s_ticket, s_flag;
+  __shared__ unsigned int s_ticket;
+  __shared__ uint32_t s_wmax[W];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int ld = lane % LD, ll = lane / LD;
   const uint32_t tag = static_cast<uint32_t>(p.k);
 
-  if (tid == 0) {
-    s_ticket = atomicAdd(p.ctr + (p.k - 1), 1u);
-    // the stop flag was written by an earlier launch on the same stream
-    s_flag = (p.early_exit && p.k > 1)
-                 ? __hip_atomic_load(p.ctr + 2 * p.K, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                 : 0u;
-  }
+  if (tid == 0) s_ticket = atomicAdd(p.ctr + (p.k - 1), 1u);
   __syncthreads();
+  bool skip = false;
+  if (p.early_exit && p.k > 1) {
+    // early exit: once every row's update of the previous launch is within tol
+    // (skipped launches leave their row maxima at 0), this launch only carries
+    // the iterate forward. The previous launch finished before this one began.
+    int ok = 1;
+    for (int bb = tid; bb < p.B; bb += blockDim.x)
+      ok &= (__uint_as_float(p.maxupd[static_cast<long long>(p.k - 2) * p.B + bb]) <= p.tol) ? 1 : 0;
+    skip = __syncthreads_and(ok) != 0;
+  }
   const unsigned int ticket = s_ticket;
   const unsigned int ntiles = static_cast<unsigned int>(p.B) * p.ntiles_d;
   const int chunk = static_cast<int>(ticket / ntiles);
@@ -165,10 +168,28 @@ __global__ void __launch_bounds__(64 * W) newton_iter_kernel(const IterArgs p) {
   const int l0 = chunk * CL + (wave * LL + ll) * T;
   const long long BD = static_cast<long long>(p.B) * p.D;
   const long long chan = static_cast<long long>(b) * p.D + d0;
-  const long long row0 = static_cast<long long>(b) * p.L;  // (b, l) -> (row0 + l) * D + d
-  const UT* __restrict__ u = static_cast<const UT*>(p.u);
+  // Addressing: workgroup-uniform 64-bit bases (scalar registers) plus 32-bit
+  // per-lane byte offsets; a timestep advances the state by D floats and the
+  // gate inputs by G*D elements.
+  const int dt0 = (tile - b * p.ntiles_d) * CW;
+  const long long wrow = static_cast<long long>(b) * p.L + static_cast<long long>(chunk) * CL;
+  const char* __restrict__ ubase =
+      reinterpret_cast<const char*>(p.u) + (wrow * G * p.D + dt0) * static_cast<long long>(sizeof(UT));
+  const long long sdelta = (wrow * p.D + dt0) * static_cast<long long>(sizeof(float));
+  const int lt0 = (wave * LL + ll) * T;  // lane's first timestep within the chunk
+  const uint32_t ustep = static_cast<uint32_t>(G * p.D * sizeof(UT));
+  const uint32_t gstep = static_cast<uint32_t>(p.D * sizeof(UT));
+  const uint32_t sstep = static_cast<uint32_t>(p.D * sizeof(float));
+  const uint32_t uoff = static_cast<uint32_t>(lt0) * ustep + static_cast<uint32_t>(ld * C * sizeof(UT));
+  const uint32_t soff = static_cast<uint32_t>(lt0) * sstep + static_cast<uint32_t>(ld * C * sizeof(float));
+  auto sptr_in = [&](int s, uint32_t off) {
+    return reinterpret_cast<const float*>(reinterpret_cast<const char*>(p.sin[s]) + sdelta + off);
+  };
+  auto sptr_out = [&](int s, uint32_t off) {
+    return reinterpret_cast<float*>(reinterpret_cast<char*>(p.sout[s]) + sdelta + off);
+  };
 
-  if (s_flag) {
+  if (skip) {
     // early exit fired earlier: keep the converged iterate, moved to this launch's output
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -177,8 +198,8 @@ __global__ void __launch_bounds__(64 * W) newton_iter_kernel(const IterArgs p) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
           float v[C];
-          ld_f32<C>(p.sin[s] + (row0 + l) * p.D + d0, v);
-          st_f32<C>(p.sout[s] + (row0 + l) * p.D + d0, v);
+          ld_f32<C>(sptr_in(s, soff + t * sstep), v);
+          st_f32<C>(sptr_out(s, soff + t * sstep), v);
         }
       }
     }
@@ -186,45 +207,46 @@ __global__ void __launch_bounds__(64 * W) newton_iter_kernel(const IterArgs p) {
   }
 
   // ---- a1: stream gate inputs and the previous iterate -------------------
+  // Loads are unconditional: rows beyond L are clamped to the last row and
+  // channel groups beyond D to the last group, so every address is inside the
+  // tensors. Such steps only follow every valid step of their channel in scan
+  // order, so their (J, r) never reach a stored value.
+  const int lastrow = p.L - 1 - chunk * CL;                // >= 0: the chunk holds a valid row
+  const int dcl = (dv ? d0 : p.D - C) - dt0;               // >= 0: the tile holds a valid group
+  const int dc = dt0 + dcl;                                // clamped channel
   float av[G][C];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    if (dv) ld_f32<C>(p.a + static_cast<long long>(g) * p.D + d0, av[g]);
-    else
-#pragma unroll
-      for (int c = 0; c < C; ++c) av[g][c] = 0.0f;
-  }
+  for (int g = 0; g < G; ++g) ld_f32<C>(p.a + static_cast<long long>(g) * p.D + dc, av[g]);
   float sp[NS][C];  // iterate k-1 at l0 - 1 (the initial state at l0 == 0)
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
+    float v0[C], v1[C];
 #pragma unroll
-    for (int c = 0; c < C; ++c) sp[s][c] = 0.0f;
-    if (dv) {
-      if (l0 == 0) {
-        if (p.s0[s]) ld_f32<C>(p.s0[s] + static_cast<long long>(b) * p.D + d0, sp[s]);
-      } else if (p.sin[s] && l0 <= p.L) {
-        ld_f32<C>(p.sin[s] + (row0 + l0 - 1) * p.D + d0, sp[s]);
-      }
+    for (int c = 0; c < C; ++c) v0[c] = v1[c] = 0.0f;
+    if (p.s0[s]) ld_f32<C>(p.s0[s] + static_cast<long long>(b) * p.D + dc, v0);
+    if (p.sin[s]) {
+      const long long prow = wrow + min(max(lt0 - 1, -chunk * CL), lastrow);  // >= 0
+      ld_f32<C>(p.sin[s] + prow * p.D + dc, v1);
     }
+#pragma unroll
+    for (int c = 0; c < C; ++c) sp[s][c] = (l0 == 0) ? v0[c] : v1[c];
   }
   float so[T][NS][C];
   URaw<UT, C> uu[T][G];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
-    const int l = l0 + t;
-    const bool v = dv && l < p.L;
+    const uint32_t rr = static_cast<uint32_t>(min(lt0 + t, lastrow));
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      if (v && p.sin[s]) ld_f32<C>(p.sin[s] + (row0 + l) * p.D + d0, so[t][s]);
+      if (p.sin[s]) ld_f32_stream<C>(sptr_in(s, rr * sstep + static_cast<uint32_t>(dcl * sizeof(float))), so[t][s]);
       else
 #pragma unroll
         for (int c = 0; c < C; ++c) so[t][s][c] = 0.0f;
     }
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      if (v) uu[t][g].load(u + ((row0 + l) * G + g) * p.D + d0);
-      else uu[t][g].zero();
-    }
+    for (int g = 0; g < G; ++g)
+      uu[t][g].load(reinterpret_cast<const UT*>(
+          ubase + static_cast<uint32_t>(rr * ustep + g * gstep + static_cast<uint32_t>(dcl * sizeof(UT)))));
   }
 
   // ---- a2 + a3: residual and Jacobian per step; serial scan of the lane's T steps
@@ -233,7 +255,6 @@ __global__ void __launch_bounds__(64 * W) newton_iter_kernel(const IterArgs p) {
   acc.set_identity();
 #pragma unroll
   for (int t = 0; t < T; ++t) {
-    const bool v = dv && (l0 + t) < p.L;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       float ac[G], uc[G], pc[NS], f[NS], J[NS][NS];
@@ -245,21 +266,11 @@ __global__ void __launch_bounds__(64 * W) newton_iter_kernel(const IterArgs p) {
 #pragma unroll
       for (int r = 0; r < NS; ++r) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) Jt[t][r][s][c] = v ? J[r][s] : (r == s ? 1.0f : 0.0f);
-        rt[t][r][c] = v ? (f[r] - so[t][r][c]) : 0.0f;
+        for (int s = 0; s < NS; ++s) Jt[t][r][s][c] = J[r][s];
+        rt[t][r][c] = f[r] - so[t][r][c];
       }
     }
-    Aff<NS, C> e;
-#pragma unroll
-    for (int r = 0; r < NS; ++r)
-#pragma unroll
-      for (int c = 0; c < C; ++c) {
-#pragma unroll
-        for (int s = 0; s < NS; ++s) e.A[r][s][c] = Jt[t][r][s][c];
-        e.b[r][c] = rt[t][r][c];
-      }
-    e.after(acc);
-    acc = e;
+    acc.pre(Jt[t], rt[t]);
   }
 
   // ---- a4: scan across the LL lane groups of the wave (shuffles) -----------
@@ -378,42 +389,75 @@ __global__ void __launch_bounds__(64 * W) newton_iter_kernel(const IterArgs p) {
           o[c] = so[t][r][c] + x[r][c];
           mbits = max(mbits, __float_as_uint(fabsf(x[r][c])));
         }
-        st_f32<C>(p.sout[r] + (row0 + l) * p.D + d0, o);
+        st_f32<C>(sptr_out(r, soff + t * sstep), o);
       }
     }
   }
   // row max of |update|: wave reduction on the bit patterns (NaN ranks above +inf)
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mbits = max(mbits, static_cast<uint32_t>(__shfl_xor(mbits, off, 64)));
-  if (lane == 0) atomicMax(p.maxupd + static_cast<long long>(p.k - 1) * p.B + b, mbits);
-
-  // ---- flags: the last workgroup of the launch turns row maxima into flags
+  // workgroup max, one plain store per workgroup (same-address atomics from
+  // every wave would serialise at the device coherence point)
+  if (lane == 0) s_wmax[wave] = mbits;
   __syncthreads();
   if (tid == 0) {
-    __threadfence();
-    const unsigned int n = atomicAdd(p.ctr + p.K + (p.k - 1), 1u);
-    s_flag = (n == gridDim.x - 1) ? 1u : 0u;
+    uint32_t m = s_wmax[0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) m = max(m, s_wmax[w]);
+    p.pmax[static_cast<long long>(p.k - 1) * gridDim.x + ticket] = m;
   }
+}
+
+// Row maxima of |update| for iterations [k0, k0 + gridDim.y): block (b, k)
+// reduces the per-workgroup partials of row b. Workgroup ticket t covers
+// chunk t / (B * ntiles_d) and tile t % (B * ntiles_d), whose row is tile / ntiles_d.
+__global__ void __launch_bounds__(256) rowmax_kernel(const unsigned int* pmax, unsigned int* maxupd, int B,
+                                                     int ntiles_d, int nchunks, int k0) {
+  __shared__ uint32_t s_red[256];
+  const int b = blockIdx.x, k = k0 + blockIdx.y;
+  const long long nwg = static_cast<long long>(B) * ntiles_d * nchunks;
+  const int per_row = ntiles_d * nchunks;
+  uint32_t m = 0u;
+  for (int i = threadIdx.x; i < per_row; i += blockDim.x) {
+    const int chunk = i / ntiles_d, dt = i - chunk * ntiles_d;
+    const long long t = static_cast<long long>(chunk) * B * ntiles_d + static_cast<long long>(b) * ntiles_d + dt;
+    m = max(m, pmax[static_cast<long long>(k) * nwg + t]);
+  }
+  s_red[threadIdx.x] = m;
   __syncthreads();
-  if (s_flag) {
-    __threadfence();
-    int allc = 1;
-    for (int bb = tid; bb < p.B; bb += blockDim.x) {
-      const uint32_t mb = __hip_atomic_load(p.maxupd + static_cast<long long>(p.k - 1) * p.B + bb,
-                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const float mf = __uint_as_float(mb);
-      const int cv = (mf <= p.tol) ? 1 : 0;  // NaN compares false
-      if (p.maxupd_out) p.maxupd_out[static_cast<long long>(p.k - 1) * p.B + bb] = mf;
-      if (p.conv_out) p.conv_out[bb] = cv;
-      allc &= cv;
-    }
-    allc = __syncthreads_and(allc);
-    if (tid == 0) {
-      const bool stop = p.early_exit && allc;
-      if (p.iters_out && (stop || p.k == p.K)) *p.iters_out = p.k;
-      if (stop) __hip_atomic_store(p.ctr + 2 * p.K, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int off = blockDim.x / 2; off > 0; off >>= 1) {
+    if (threadIdx.x < off) s_red[threadIdx.x] = max(s_red[threadIdx.x], s_red[threadIdx.x + off]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) maxupd[static_cast<long long>(k) * B + b] = s_red[0];
+}
+
+// After the last iteration: iteration count and per-row convergence flags from
+// the row maxima (one workgroup; also copies the row maxima out as floats).
+__global__ void __launch_bounds__(256) newton_flags_kernel(const unsigned int* maxupd, int B, int K,
+                                                           float tol, int early_exit, int32_t* iters_out,
+                                                           int32_t* conv_out, float* maxupd_out) {
+  const int tid = threadIdx.x;
+  int iters = K;
+  if (early_exit) {
+    for (int k = 1; k <= K; ++k) {
+      int ok = 1;
+      for (int b = tid; b < B; b += blockDim.x)
+        ok &= (__uint_as_float(maxupd[static_cast<long long>(k - 1) * B + b]) <= tol) ? 1 : 0;
+      if (__syncthreads_and(ok)) {
+        iters = k;
+        break;
+      }
     }
   }
+  for (int b = tid; b < B; b += blockDim.x) {
+    if (conv_out)
+      conv_out[b] = (__uint_as_float(maxupd[static_cast<long long>(iters - 1) * B + b]) <= tol) ? 1 : 0;
+  }
+  if (maxupd_out)
+    for (long long i = tid; i < static_cast<long long>(K) * B; i += blockDim.x)
+      maxupd_out[i] = __uint_as_float(maxupd[i]);
+  if (iters_out && tid == 0) *iters_out = iters;
 }
 
 // Clears the zero-initialised part of the workspace (counters, row maxima,

@@ -14,47 +14,68 @@ namespace pararnn {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Launch configurations. Per (cell, C): T timesteps per lane, W waves per
-// workgroup, LL lane groups along L per wave. The chunk length W*LL*T is fixed
-// per cell and operation so that the workspace size does not depend on C.
+// Launch configurations. Per (cell, C, operation): T timesteps per lane, W
+// waves per workgroup, LL lane groups along L per wave; a workgroup covers
+// (64/LL)*C channels x W*LL*T timesteps (one chunk of the look-back). The
+// LSTM keeps at most two channels per lane (six scan values per channel).
 template <class Cell, int C, bool ADJ>
 struct Cfg;
-// ParaGRU forward: chunk 128 timesteps
 template <> struct Cfg<GruCell, 4, false> { static constexpr int T = 8, W = 4, LL = 4; };
 template <> struct Cfg<GruCell, 2, false> { static constexpr int T = 8, W = 8, LL = 2; };
 template <> struct Cfg<GruCell, 1, false> { static constexpr int T = 16, W = 8, LL = 1; };
-// ParaLSTM forward: chunk 128
-template <> struct Cfg<LstmCell, 4, false> { static constexpr int T = 4, W = 8, LL = 4; };
-template <> struct Cfg<LstmCell, 2, false> { static constexpr int T = 8, W = 4, LL = 4; };
-template <> struct Cfg<LstmCell, 1, false> { static constexpr int T = 16, W = 8, LL = 1; };
-// adjoints: chunk 128
+template <> struct Cfg<LstmCell, 1, false> { static constexpr int T = 16, W = 4, LL = 2; };
 template <> struct Cfg<GruCell, 4, true> { static constexpr int T = 4, W = 8, LL = 4; };
 template <> struct Cfg<GruCell, 2, true> { static constexpr int T = 8, W = 4, LL = 4; };
 template <> struct Cfg<GruCell, 1, true> { static constexpr int T = 8, W = 8, LL = 2; };
-template <> struct Cfg<LstmCell, 4, true> { static constexpr int T = 4, W = 8, LL = 4; };
-template <> struct Cfg<LstmCell, 2, true> { static constexpr int T = 4, W = 8, LL = 4; };
+template <> struct Cfg<LstmCell, 2, true> { static constexpr int T = 16, W = 4, LL = 1; };
 template <> struct Cfg<LstmCell, 1, true> { static constexpr int T = 8, W = 8, LL = 2; };
 
-constexpr int kChunk = 128;
+// widest channel group per lane: the LSTM Newton iteration runs one channel
+// per lane (its per-step 2x2 Jacobian, residual and previous iterate leave no
+// registers for more), the LSTM adjoint two
+template <class Cell, bool ADJ> constexpr int max_c() { return Cell::NS == 2 ? (ADJ ? 2 : 1) : 4; }
+
+// workgroup footprint of one configuration: timesteps (one look-back chunk)
+// and channels
+struct Geo {
+  int chunk, cw;
+};
 
 template <class Cell, int C, bool ADJ>
-constexpr int chunk_len() {
-  return Cfg<Cell, C, ADJ>::T * Cfg<Cell, C, ADJ>::W * Cfg<Cell, C, ADJ>::LL;
+constexpr Geo geo() {
+  using K = Cfg<Cell, C, ADJ>;
+  return Geo{K::T * K::W * K::LL, (64 / K::LL) * C};
 }
-static_assert(chunk_len<GruCell, 4, false>() == kChunk && chunk_len<GruCell, 2, false>() == kChunk &&
-                  chunk_len<GruCell, 1, false>() == kChunk && chunk_len<LstmCell, 4, false>() == kChunk &&
-                  chunk_len<LstmCell, 2, false>() == kChunk && chunk_len<LstmCell, 1, false>() == kChunk &&
-                  chunk_len<GruCell, 4, true>() == kChunk && chunk_len<GruCell, 2, true>() == kChunk &&
-                  chunk_len<GruCell, 1, true>() == kChunk && chunk_len<LstmCell, 4, true>() == kChunk &&
-                  chunk_len<LstmCell, 2, true>() == kChunk && chunk_len<LstmCell, 1, true>() == kChunk,
-              "every configuration must cover kChunk timesteps per workgroup");
+
+template <class Cell, bool ADJ>
+Geo geo_for_c(int C) {
+  if constexpr (max_c<Cell, ADJ>() >= 4) {
+    if (C == 4) return geo<Cell, 4, ADJ>();
+  }
+  if constexpr (max_c<Cell, ADJ>() >= 2) {
+    if (C == 2) return geo<Cell, 2, ADJ>();
+  }
+  return geo<Cell, 1, ADJ>();
+}
+
+Geo geo_for(int cell, int op, int C) {
+  const bool adj = op == PARARNN_OP_ADJOINT;
+  if (cell == PARARNN_LSTM) return adj ? geo_for_c<LstmCell, true>(C) : geo_for_c<LstmCell, false>(C);
+  return adj ? geo_for_c<GruCell, true>(C) : geo_for_c<GruCell, false>(C);
+}
+
+int cmax_for(int cell, int op) {
+  const bool adj = op == PARARNN_OP_ADJOINT;
+  if (cell == PARARNN_LSTM) return adj ? max_c<LstmCell, true>() : max_c<LstmCell, false>();
+  return adj ? max_c<GruCell, true>() : max_c<GruCell, false>();
+}
 
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t ctr = 0, maxupd = 0, incl = 0, agg = 0, dapart = 0, zero_end = 0, state = 0, total = 0;
-  int nchunks = 0;
+  size_t ctr = 0, maxupd = 0, pmax = 0, incl = 0, agg = 0, dapart = 0, zero_end = 0, state = 0, total = 0;
+  int nchunks = 0, ntiles_d = 0;
 };
 
 int nstate(int cell) { return cell == PARARNN_LSTM ? 2 : 1; }
@@ -69,24 +90,31 @@ bool opts_ok(int cell, int op, const pararnn_opts* o) {
   // element counts must stay addressable with 64-bit offsets and tickets in 32 bits
   const double n = static_cast<double>(o->B) * o->L * o->D * 4;
   if (n > 9.0e18) return false;
-  const double wgs = static_cast<double>(o->B) * ((o->D + 15) / 16) * ((o->L + kChunk - 1) / kChunk);
-  if (wgs > 2.0e9) return false;
+  for (int C = 1; C <= cmax_for(cell, op); C *= 2) {
+    const Geo g = geo_for(cell, op, C);
+    const double wgs = static_cast<double>(o->B) * ((o->D + g.cw - 1) / g.cw) * ((o->L + g.chunk - 1) / g.chunk);
+    if (wgs > 2.0e9) return false;
+  }
   return true;
 }
 
 // Workspace: [counters | row maxima | incl descriptors | agg descriptors | da partials]
 // (cleared at the start of every call) followed by the ping-pong state buffer.
-Layout layout(int cell, int op, const pararnn_opts* o, bool with_da) {
+Layout layout(int cell, int op, const pararnn_opts* o, bool with_da, Geo g) {
   Layout y;
   const int NS = nstate(cell), G = ngates(cell);
   const size_t B = o->B, L = o->L, D = o->D;
   const int K = (op == PARARNN_OP_SOLVE) ? o->max_iters : 1;
-  y.nchunks = static_cast<int>((L + kChunk - 1) / kChunk);
+  y.nchunks = static_cast<int>((L + g.chunk - 1) / g.chunk);
+  y.ntiles_d = static_cast<int>((D + g.cw - 1) / g.cw);
+  const size_t nwg = B * static_cast<size_t>(y.ntiles_d) * y.nchunks;
   size_t off = 0;
   y.ctr = off;
-  off = round_up(off + sizeof(uint32_t) * (2 * K + 1));
+  off = round_up(off + sizeof(uint32_t) * K);
   y.maxupd = off;
   off = round_up(off + sizeof(uint32_t) * static_cast<size_t>(K) * B);
+  y.pmax = off;
+  if (op == PARARNN_OP_SOLVE) off = round_up(off + sizeof(uint32_t) * static_cast<size_t>(K) * nwg);
   y.incl = off;
   if (y.nchunks > 1) off = round_up(off + sizeof(uint64_t) * y.nchunks * NS * B * D);
   y.agg = off;
@@ -136,11 +164,8 @@ int clear_ws(char* ws, const Layout& y, float* user, long long nuser, hipStream_
 template <class Cell, class UT, int C>
 int launch_iter(const IterArgs& a, hipStream_t s) {
   using K = Cfg<Cell, C, false>;
-  constexpr int CW = (64 / K::LL) * C;
-  const unsigned ntiles_d = static_cast<unsigned>((a.D + CW - 1) / CW);
-  const unsigned grid = static_cast<unsigned>(a.B) * ntiles_d * static_cast<unsigned>(a.nchunks);
-  IterArgs b = a;
-  b.ntiles_d = static_cast<int>(ntiles_d);
+  const unsigned grid = static_cast<unsigned>(a.B) * a.ntiles_d * static_cast<unsigned>(a.nchunks);
+  const IterArgs& b = a;
   hipLaunchKernelGGL((newton_iter_kernel<Cell, UT, C, K::T, K::W, K::LL>), dim3(grid), dim3(64 * K::W), 0,
                      s, b);
   return check_hip(hipGetLastError());
@@ -148,38 +173,35 @@ int launch_iter(const IterArgs& a, hipStream_t s) {
 
 template <class Cell, class UT>
 int launch_iter_c(int C, const IterArgs& a, hipStream_t s) {
-  switch (C) {
-    case 4: return launch_iter<Cell, UT, 4>(a, s);
-    case 2: return launch_iter<Cell, UT, 2>(a, s);
-    default: return launch_iter<Cell, UT, 1>(a, s);
+  if constexpr (max_c<Cell, false>() >= 4) {
+    if (C == 4) return launch_iter<Cell, UT, 4>(a, s);
   }
+  if constexpr (max_c<Cell, false>() >= 2) {
+    if (C == 2) return launch_iter<Cell, UT, 2>(a, s);
+  }
+  return launch_iter<Cell, UT, 1>(a, s);
 }
 
 template <class Cell>
 int launch_iter_any(int dtype, int C, const IterArgs& a, hipStream_t s) {
-  if constexpr (Cell::NS == 2) C = C > 2 ? 2 : C;
   return dtype == PARARNN_BF16 ? launch_iter_c<Cell, bf16>(C, a, s) : launch_iter_c<Cell, float>(C, a, s);
 }
 
 template <class Cell, class UT, int C>
 int launch_adj(const AdjArgs& a, hipStream_t s) {
   using K = Cfg<Cell, C, true>;
-  constexpr int CW = (64 / K::LL) * C;
-  const unsigned ntiles_d = static_cast<unsigned>((a.D + CW - 1) / CW);
-  const unsigned grid = static_cast<unsigned>(a.B) * ntiles_d * static_cast<unsigned>(a.nchunks);
-  AdjArgs b = a;
-  b.ntiles_d = static_cast<int>(ntiles_d);
+  const unsigned grid = static_cast<unsigned>(a.B) * a.ntiles_d * static_cast<unsigned>(a.nchunks);
+  const AdjArgs& b = a;
   hipLaunchKernelGGL((adjoint_kernel<Cell, UT, C, K::T, K::W, K::LL>), dim3(grid), dim3(64 * K::W), 0, s, b);
   return check_hip(hipGetLastError());
 }
 
 template <class Cell, class UT>
 int launch_adj_c(int C, const AdjArgs& a, hipStream_t s) {
-  switch (C) {
-    case 4: return launch_adj<Cell, UT, 4>(a, s);
-    case 2: return launch_adj<Cell, UT, 2>(a, s);
-    default: return launch_adj<Cell, UT, 1>(a, s);
+  if constexpr (max_c<Cell, true>() >= 4) {
+    if (C == 4) return launch_adj<Cell, UT, 4>(a, s);
   }
+  return C == 2 ? launch_adj<Cell, UT, 2>(a, s) : launch_adj<Cell, UT, 1>(a, s);
 }
 
 template <class Cell>
@@ -194,12 +216,15 @@ int solve(int cell, const void* u, const float* a, const float* c0, const float*
   if (!u || !a || !h || !ws || (cell == PARARNN_LSTM && !c)) return PARARNN_EINVAL;
   if (o->u_dtype != PARARNN_F32 && o->u_dtype != PARARNN_BF16) return PARARNN_EUNSUPPORTED;
   if (o->early_exit != 0 && o->early_exit != 1) return PARARNN_EINVAL;
-  const Layout y = layout(cell, PARARNN_OP_SOLVE, o, false);
+  const size_t usize = o->u_dtype == PARARNN_BF16 ? 2 : 4;
+  const int C = pick_c(cmax_for(cell, PARARNN_OP_SOLVE), o->D, usize, u, {a, h0, h, c0, c});
+  if (!C || !aligned(u, usize)) return PARARNN_EUNSUPPORTED;
+  const Geo g = geo_for(cell, PARARNN_OP_SOLVE, C);
+  // per-lane offsets inside one chunk of gate inputs are 32-bit
+  if (static_cast<double>(g.chunk) * ngates(cell) * o->D * 4.0 >= 2147483648.0) return PARARNN_EUNSUPPORTED;
+  const Layout y = layout(cell, PARARNN_OP_SOLVE, o, false, g);
   if (ws_bytes < y.total) return PARARNN_EWORKSPACE;
   if (!aligned(ws, kAlign)) return PARARNN_EUNSUPPORTED;
-  const size_t usize = o->u_dtype == PARARNN_BF16 ? 2 : 4;
-  const int C = pick_c(cell == PARARNN_LSTM ? 2 : 4, o->D, usize, u, {a, h0, h, c0, c});
-  if (!C || !aligned(u, usize)) return PARARNN_EUNSUPPORTED;
 
   const int K = o->max_iters, NS = nstate(cell);
   const size_t BLD = static_cast<size_t>(o->B) * o->L * o->D;
@@ -210,7 +235,7 @@ int solve(int cell, const void* u, const float* a, const float* c0, const float*
 
   int rc = record(o, 0, stream);
   if (rc) return rc;
-  rc = clear_ws(w, y, max_update, max_update ? static_cast<long long>(K) * o->B : 0, stream);
+  rc = clear_ws(w, y, nullptr, 0, stream);
   if (rc) return rc;
   rc = record(o, 1, stream);
   if (rc) return rc;
@@ -225,9 +250,8 @@ int solve(int cell, const void* u, const float* a, const float* c0, const float*
   ia.agg = reinterpret_cast<unsigned long long*>(w + y.agg);
   ia.ctr = reinterpret_cast<unsigned int*>(w + y.ctr);
   ia.maxupd = reinterpret_cast<unsigned int*>(w + y.maxupd);
-  ia.iters_out = iters;
-  ia.conv_out = converged;
-  ia.maxupd_out = max_update;
+  ia.pmax = reinterpret_cast<unsigned int*>(w + y.pmax);
+  ia.ntiles_d = y.ntiles_d;
   ia.B = o->B;
   ia.L = o->L;
   ia.D = o->D;
@@ -248,8 +272,23 @@ int solve(int cell, const void* u, const float* a, const float* c0, const float*
     if (rc) return rc;
     rc = record(o, k + 1, stream);
     if (rc) return rc;
+    if (o->early_exit) {  // the next launch decides from this launch's row maxima
+      hipLaunchKernelGGL(rowmax_kernel, dim3(o->B, 1), dim3(256), 0, stream, ia.pmax, ia.maxupd, o->B,
+                         y.ntiles_d, y.nchunks, k - 1);
+      rc = check_hip(hipGetLastError());
+      if (rc) return rc;
+    }
   }
-  return PARARNN_OK;
+  if (!o->early_exit) {
+    hipLaunchKernelGGL(rowmax_kernel, dim3(o->B, K), dim3(256), 0, stream, ia.pmax, ia.maxupd, o->B, y.ntiles_d,
+                       y.nchunks, 0);
+    rc = check_hip(hipGetLastError());
+    if (rc) return rc;
+  }
+  hipLaunchKernelGGL(newton_flags_kernel, dim3(1), dim3(256), 0, stream,
+                     static_cast<const unsigned int*>(ia.maxupd), o->B, K, o->tol, o->early_exit, iters,
+                     converged, max_update);
+  return check_hip(hipGetLastError());
 }
 
 }  // namespace
@@ -259,7 +298,12 @@ using namespace pararnn;
 
 extern "C" size_t pararnn_workspace_bytes(int32_t cell, int32_t op, const pararnn_opts* o) {
   if (!opts_ok(cell, op, o)) return 0;
-  return layout(cell, op, o, true).total;
+  size_t n = 0;
+  for (int C = 1; C <= cmax_for(cell, op); C *= 2) {
+    const size_t t = layout(cell, op, o, true, geo_for(cell, op, C)).total;
+    n = t > n ? t : n;
+  }
+  return n;
 }
 
 extern "C" int32_t pararnn_solve_gru(const void* u, const float* a, const float* h0, float* h, void* ws,
@@ -284,14 +328,14 @@ extern "C" int32_t pararnn_adjoint(int32_t cell, const void* u, const float* a, 
   if (!opts_ok(cell, PARARNN_OP_ADJOINT, o)) return PARARNN_EINVAL;
   if (!u || !a || !h || !dh || !du || !ws || (cell == PARARNN_LSTM && !c)) return PARARNN_EINVAL;
   if (o->u_dtype != PARARNN_F32 && o->u_dtype != PARARNN_BF16) return PARARNN_EUNSUPPORTED;
-  const Layout y = layout(cell, PARARNN_OP_ADJOINT, o, da != nullptr);
-  if (ws_bytes < y.total) return PARARNN_EWORKSPACE;
-  if (!aligned(ws, kAlign)) return PARARNN_EUNSUPPORTED;
   const size_t usize = o->u_dtype == PARARNN_BF16 ? 2 : 4;
   const bool lstm = cell == PARARNN_LSTM;
-  const int C = pick_c(lstm ? 2 : 4, o->D, usize, u,
+  const int C = pick_c(cmax_for(cell, PARARNN_OP_ADJOINT), o->D, usize, u,
                       {a, h0, h, dh, du, ds0, da, lstm ? c0 : nullptr, lstm ? c : nullptr});
   if (!C || !aligned(u, usize)) return PARARNN_EUNSUPPORTED;
+  const Layout y = layout(cell, PARARNN_OP_ADJOINT, o, da != nullptr, geo_for(cell, PARARNN_OP_ADJOINT, C));
+  if (ws_bytes < y.total) return PARARNN_EWORKSPACE;
+  if (!aligned(ws, kAlign)) return PARARNN_EUNSUPPORTED;
   char* w = static_cast<char*>(ws);
 
   int rc = record(o, 0, stream);
@@ -320,6 +364,7 @@ extern "C" int32_t pararnn_adjoint(int32_t cell, const void* u, const float* a, 
   aa.L = o->L;
   aa.D = o->D;
   aa.nchunks = y.nchunks;
+  aa.ntiles_d = y.ntiles_d;
   rc = lstm ? launch_adj_any<LstmCell>(o->u_dtype, C, aa, stream)
             : launch_adj_any<GruCell>(o->u_dtype, C, aa, stream);
   if (rc) return rc;
