@@ -79,9 +79,13 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
+def traffic_path(workload: str) -> Path:
+    return ROOT / "profiles" / f"newton_iter_{workload}_traffic.json"
+
+
 def load_traffic(workload: str, digest: str):
     """Counter-measured HBM bytes per launch for the current kernel sources, if profiled."""
-    f = ROOT / "profiles" / f"newton_iter_{workload}_traffic.json"
+    f = traffic_path(workload)
     if not f.exists():
         return None
     try:
@@ -91,6 +95,38 @@ def load_traffic(workload: str, digest: str):
     if d.get("source_digest") != digest:
         return None
     return d.get("bytes_per_launch")
+
+
+def traffic_from_counters(workload: str, fetch_csv: str, write_csv: str, iters: int) -> dict:
+    """Per-launch HBM bytes of the Newton-iteration kernel from two rocprofv3
+    --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) of
+    `bench.py --copy-calibration`. Each counter is scaled by bytes / counter of
+    the 1 GiB device copy in the same run."""
+    import csv
+
+    def read(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        copy = [float(r["Counter_Value"]) * 1024 for r in rows
+                if "copyBuffer" in r["Kernel_Name"] and float(r["Counter_Value"]) > 1e5]
+        its = [float(r["Counter_Value"]) * 1024 for r in rows if "newton_iter_kernel" in r["Kernel_Name"]]
+        return copy, its
+
+    calib = float(1 << 30)
+    fc, fi = read(fetch_csv, "FETCH_SIZE")
+    wc, wi = read(write_csv, "WRITE_SIZE")
+    fscale = calib / (sum(fc) / len(fc))
+    wscale = calib / (sum(wc) / len(wc))
+    # dispatches come in solves of `iters` launches; average each launch index
+    per_k = []
+    for k in range(iters):
+        f = [v * fscale for j, v in enumerate(fi) if j % iters == k]
+        w = [v * wscale for j, v in enumerate(wi) if j % iters == k]
+        per_k.append({"fetch": sum(f) / len(f), "write": sum(w) / len(w)})
+    mean = sum(x["fetch"] + x["write"] for x in per_k) / iters
+    return {"workload": workload, "source_digest": source_digest(), "bytes_per_launch": mean,
+            "per_launch": per_k, "fetch_scale": fscale, "write_scale": wscale,
+            "calibration": "1 GiB hipMemcpy device copy (__amd_rocclr_copyBuffer) in the same run"}
 
 
 def cpu_baseline(w, x, iters, target_s=12.0):
@@ -139,7 +175,17 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration for profiling)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/newton_iter_<workload>_traffic.json from rocprofv3 counter CSVs")
     args = ap.parse_args(argv)
+    if args.traffic_from:
+        sys.path.insert(0, str(ROOT))
+        from nonlinear_rnn_solve_newton_amd.workloads import HEADLINE, WORKLOADS
+        w = WORKLOADS[args.workload or HEADLINE]
+        d = traffic_from_counters(w.name, *args.traffic_from, iters=w.iters)
+        traffic_path(w.name).write_text(json.dumps(d, indent=1) + "\n")
+        print(json.dumps(d))
+        return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build runs on one GPU only; the multi-GPU sharding is a design "
                                    "note, not an implementation", "n_gpus": args.gpus}))

@@ -63,8 +63,8 @@ __global__ void __launch_bounds__(64 * W) adjoint_kernel(const AdjArgs p) {
   const bool dv = d0 < p.D;
   const int q = wave * LL + ll;          // position in scan order (from the end)
   const int l0 = chunk * CL + (NSEG - 1 - q) * T;
-  const long long BD = static_cast<long long>(p.B) * p.D;
-  const long long chan = static_cast<long long>(b) * p.D + d0;
+  const long long BD = static_cast<long long>(p.B) * p.ntiles_d * CW;  // descriptor slots per component
+  const long long chan = static_cast<long long>(tile) * CW + ld;
   const long long row0 = static_cast<long long>(b) * p.L;
   const UT* __restrict__ u = static_cast<const UT*>(p.u);
 
@@ -204,8 +204,8 @@ __global__ void __launch_bounds__(64 * W) adjoint_kernel(const AdjArgs p) {
         tot = e;
       }
       if (chunk < p.nchunks - 1) {
-        if (chunk > 0) publish_agg<NS, C>(p.agg, BD, chan, chunk, tag, tot);
-        lookback<NS, C>(p.incl, p.agg, BD, chan, chunk, +1, p.nchunks, tag, carry);
+        if (chunk > 0) publish_agg<NS, C>(p.agg, BD, chan, LD, chunk, tag, tot);
+        lookback<NS, C>(p.incl, p.agg, BD, chan, LD, chunk, +1, p.nchunks, tag, carry);
       }
       if (chunk > 0) {
         float x[NS][C];
@@ -214,7 +214,7 @@ __global__ void __launch_bounds__(64 * W) adjoint_kernel(const AdjArgs p) {
 #pragma unroll
           for (int c = 0; c < C; ++c) x[s][c] = carry[s][c];
         tot.apply(x);
-        publish_incl<NS, C>(p.incl, BD, chan, chunk, tag, x);
+        publish_incl<NS, C>(p.incl, BD, chan, LD, chunk, tag, x);
       }
     }
 #pragma unroll

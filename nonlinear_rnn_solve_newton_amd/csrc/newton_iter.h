@@ -41,12 +41,17 @@ struct IterArgs {
   float tol;
 };
 
+// Descriptor layout: component q of chunk i for channel slot x lives at
+// [(i * ncomp + q) * BD + x], where the slot of a lane's channel c is
+// chan + c * cs (chan = tile * CW + lane index along D, cs = lanes along D), so
+// one store or load instruction covers consecutive words across the wave.
+//
 // Looks back over predecessor chunks (chunk + dir, chunk + 2 dir, ...) until an
 // inclusive carry is found, composing chunk transforms on the way. Returns the
 // carry entering `chunk` (zero before the first chunk in scan order).
 template <int NS, int C>
 __device__ __forceinline__ void lookback(unsigned long long* incl, unsigned long long* agg,
-                                         long long BD, long long chan, int chunk, int dir,
+                                         long long BD, long long chan, int cs, int chunk, int dir,
                                          int nchunks, uint32_t tag, float (&carry)[NS][C]) {
   constexpr int NA = NS * NS + NS;
   Aff<NS, C> M;
@@ -64,11 +69,11 @@ __device__ __forceinline__ void lookback(unsigned long long* incl, unsigned long
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
-      for (int c = 0; c < C; ++c) wi[s][c] = desc_get(incl + ((long long)i * NS + s) * BD + chan + c);
+      for (int c = 0; c < C; ++c) wi[s][c] = desc_get(incl + ((long long)i * NS + s) * BD + chan + c * cs);
 #pragma unroll
     for (int q = 0; q < NA; ++q)
 #pragma unroll
-      for (int c = 0; c < C; ++c) wa[q][c] = desc_get(agg + ((long long)i * NA + q) * BD + chan + c);
+      for (int c = 0; c < C; ++c) wa[q][c] = desc_get(agg + ((long long)i * NA + q) * BD + chan + c * cs);
     bool ok_i = true, ok_a = true;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
@@ -105,7 +110,7 @@ __device__ __forceinline__ void lookback(unsigned long long* incl, unsigned long
 }
 
 template <int NS, int C>
-__device__ __forceinline__ void publish_agg(unsigned long long* agg, long long BD, long long chan,
+__device__ __forceinline__ void publish_agg(unsigned long long* agg, long long BD, long long chan, int cs,
                                             int chunk, uint32_t tag, const Aff<NS, C>& e) {
   constexpr int NA = NS * NS + NS;
 #pragma unroll
@@ -114,18 +119,18 @@ __device__ __forceinline__ void publish_agg(unsigned long long* agg, long long B
     for (int c = 0; c < C; ++c) {
 #pragma unroll
       for (int s = 0; s < NS; ++s)
-        desc_put(agg + ((long long)chunk * NA + r * NS + s) * BD + chan + c, tag, e.A[r][s][c]);
-      desc_put(agg + ((long long)chunk * NA + NS * NS + r) * BD + chan + c, tag, e.b[r][c]);
+        desc_put(agg + ((long long)chunk * NA + r * NS + s) * BD + chan + c * cs, tag, e.A[r][s][c]);
+      desc_put(agg + ((long long)chunk * NA + NS * NS + r) * BD + chan + c * cs, tag, e.b[r][c]);
     }
 }
 
 template <int NS, int C>
-__device__ __forceinline__ void publish_incl(unsigned long long* incl, long long BD, long long chan,
+__device__ __forceinline__ void publish_incl(unsigned long long* incl, long long BD, long long chan, int cs,
                                              int chunk, uint32_t tag, const float (&x)[NS][C]) {
 #pragma unroll
   for (int s = 0; s < NS; ++s)
 #pragma unroll
-    for (int c = 0; c < C; ++c) desc_put(incl + ((long long)chunk * NS + s) * BD + chan + c, tag, x[s][c]);
+    for (int c = 0; c < C; ++c) desc_put(incl + ((long long)chunk * NS + s) * BD + chan + c * cs, tag, x[s][c]);
 }
 
 template <class Cell, class UT, int C, int T, int W, int LL>
@@ -166,8 +171,8 @@ __global__ void __launch_bounds__(64 * W) newton_iter_kernel(const IterArgs p) {
   const int d0 = (tile - b * p.ntiles_d) * CW + ld * C;
   const bool dv = d0 < p.D;  // C divides D: all C channels valid or none
   const int l0 = chunk * CL + (wave * LL + ll) * T;
-  const long long BD = static_cast<long long>(p.B) * p.D;
-  const long long chan = static_cast<long long>(b) * p.D + d0;
+  const long long BD = static_cast<long long>(p.B) * p.ntiles_d * CW;  // descriptor slots per component
+  const long long chan = static_cast<long long>(tile) * CW + ld;
   // Addressing: workgroup-uniform 64-bit bases (scalar registers) plus 32-bit
   // per-lane byte offsets; a timestep advances the state by D floats and the
   // gate inputs by G*D elements.
@@ -322,8 +327,8 @@ __global__ void __launch_bounds__(64 * W) newton_iter_kernel(const IterArgs p) {
         tot = e;
       }
       if (chunk > 0) {
-        if (chunk < p.nchunks - 1) publish_agg<NS, C>(p.agg, BD, chan, chunk, tag, tot);
-        lookback<NS, C>(p.incl, p.agg, BD, chan, chunk, -1, p.nchunks, tag, carry);
+        if (chunk < p.nchunks - 1) publish_agg<NS, C>(p.agg, BD, chan, LD, chunk, tag, tot);
+        lookback<NS, C>(p.incl, p.agg, BD, chan, LD, chunk, -1, p.nchunks, tag, carry);
       }
       if (chunk < p.nchunks - 1) {
         float x[NS][C];
@@ -332,7 +337,7 @@ __global__ void __launch_bounds__(64 * W) newton_iter_kernel(const IterArgs p) {
 #pragma unroll
           for (int c = 0; c < C; ++c) x[s][c] = carry[s][c];
         tot.apply(x);
-        publish_incl<NS, C>(p.incl, BD, chan, chunk, tag, x);
+        publish_incl<NS, C>(p.incl, BD, chan, LD, chunk, tag, x);
       }
     }
 #pragma unroll
@@ -408,13 +413,11 @@ __global__ void __launch_bounds__(64 * W) newton_iter_kernel(const IterArgs p) {
   }
 }
 
-// Row maxima of |update| for iterations [k0, k0 + gridDim.y): block (b, k)
-// reduces the per-workgroup partials of row b. Workgroup ticket t covers
+// Row max of the per-workgroup partials of iteration k for batch row b (whole
+// block participates; result valid in thread 0). Workgroup ticket t covers
 // chunk t / (B * ntiles_d) and tile t % (B * ntiles_d), whose row is tile / ntiles_d.
-__global__ void __launch_bounds__(256) rowmax_kernel(const unsigned int* pmax, unsigned int* maxupd, int B,
-                                                     int ntiles_d, int nchunks, int k0) {
-  __shared__ uint32_t s_red[256];
-  const int b = blockIdx.x, k = k0 + blockIdx.y;
+__device__ __forceinline__ uint32_t block_rowmax(const unsigned int* pmax, int B, int ntiles_d, int nchunks,
+                                                 int k, int b, uint32_t* s_red) {
   const long long nwg = static_cast<long long>(B) * ntiles_d * nchunks;
   const int per_row = ntiles_d * nchunks;
   uint32_t m = 0u;
@@ -429,35 +432,55 @@ __global__ void __launch_bounds__(256) rowmax_kernel(const unsigned int* pmax, u
     if (threadIdx.x < off) s_red[threadIdx.x] = max(s_red[threadIdx.x], s_red[threadIdx.x + off]);
     __syncthreads();
   }
-  if (threadIdx.x == 0) maxupd[static_cast<long long>(k) * B + b] = s_red[0];
+  const uint32_t r = s_red[0];
+  __syncthreads();
+  return r;
 }
 
-// After the last iteration: iteration count and per-row convergence flags from
-// the row maxima (one workgroup; also copies the row maxima out as floats).
-__global__ void __launch_bounds__(256) newton_flags_kernel(const unsigned int* maxupd, int B, int K,
-                                                           float tol, int early_exit, int32_t* iters_out,
-                                                           int32_t* conv_out, float* maxupd_out) {
-  const int tid = threadIdx.x;
+// Early-exit mode only: row maxima of iteration k, read by the next launch.
+__global__ void __launch_bounds__(256) rowmax_kernel(const unsigned int* pmax, unsigned int* maxupd, int B,
+                                                     int ntiles_d, int nchunks, int k) {
+  __shared__ uint32_t s_red[256];
+  const uint32_t m = block_rowmax(pmax, B, ntiles_d, nchunks, k, blockIdx.x, s_red);
+  if (threadIdx.x == 0) maxupd[static_cast<long long>(k) * B + blockIdx.x] = m;
+}
+
+// After the last iteration, block (b, k) per batch row and iteration: the
+// row maximum of iteration k (unless early exit already reduced it), copied
+// out as a float; the last iteration's blocks also write the row's
+// convergence flag, and block (0, K-1) the iteration count.
+__global__ void __launch_bounds__(256) newton_finalize_kernel(const unsigned int* pmax, unsigned int* maxupd,
+                                                              int B, int ntiles_d, int nchunks, int K, float tol,
+                                                              int early_exit, int32_t* iters_out,
+                                                              int32_t* conv_out, float* maxupd_out) {
+  __shared__ uint32_t s_red[256];
+  const int b = blockIdx.x, k = blockIdx.y, tid = threadIdx.x;
+  uint32_t m;
+  if (!early_exit) {
+    m = block_rowmax(pmax, B, ntiles_d, nchunks, k, b, s_red);
+    if (tid == 0) maxupd[static_cast<long long>(k) * B + b] = m;
+  } else {
+    m = maxupd[static_cast<long long>(k) * B + b];
+  }
+  if (tid == 0 && maxupd_out) maxupd_out[static_cast<long long>(k) * B + b] = __uint_as_float(m);
+  if (k != K - 1) return;
   int iters = K;
-  if (early_exit) {
-    for (int k = 1; k <= K; ++k) {
+  if (early_exit) {  // maxupd is complete: reduced after every launch
+    for (int kk = 1; kk <= K; ++kk) {
       int ok = 1;
-      for (int b = tid; b < B; b += blockDim.x)
-        ok &= (__uint_as_float(maxupd[static_cast<long long>(k - 1) * B + b]) <= tol) ? 1 : 0;
+      for (int bb = tid; bb < B; bb += blockDim.x)
+        ok &= (__uint_as_float(maxupd[static_cast<long long>(kk - 1) * B + bb]) <= tol) ? 1 : 0;
       if (__syncthreads_and(ok)) {
-        iters = k;
+        iters = kk;
         break;
       }
     }
   }
-  for (int b = tid; b < B; b += blockDim.x) {
-    if (conv_out)
-      conv_out[b] = (__uint_as_float(maxupd[static_cast<long long>(iters - 1) * B + b]) <= tol) ? 1 : 0;
+  if (tid == 0) {
+    const uint32_t mi = (iters == K) ? m : maxupd[static_cast<long long>(iters - 1) * B + b];
+    if (conv_out) conv_out[b] = (__uint_as_float(mi) <= tol) ? 1 : 0;
+    if (iters_out && b == 0) *iters_out = iters;
   }
-  if (maxupd_out)
-    for (long long i = tid; i < static_cast<long long>(K) * B; i += blockDim.x)
-      maxupd_out[i] = __uint_as_float(maxupd[i]);
-  if (iters_out && tid == 0) *iters_out = iters;
 }
 
 // Clears the zero-initialised part of the workspace (counters, row maxima,

@@ -116,9 +116,10 @@ Layout layout(int cell, int op, const pararnn_opts* o, bool with_da, Geo g) {
   y.pmax = off;
   if (op == PARARNN_OP_SOLVE) off = round_up(off + sizeof(uint32_t) * static_cast<size_t>(K) * nwg);
   y.incl = off;
-  if (y.nchunks > 1) off = round_up(off + sizeof(uint64_t) * y.nchunks * NS * B * D);
+  const size_t slots = B * static_cast<size_t>(y.ntiles_d) * g.cw;  // descriptor slots per component
+  if (y.nchunks > 1) off = round_up(off + sizeof(uint64_t) * y.nchunks * NS * slots);
   y.agg = off;
-  if (y.nchunks > 1) off = round_up(off + sizeof(uint64_t) * y.nchunks * (NS * NS + NS) * B * D);
+  if (y.nchunks > 1) off = round_up(off + sizeof(uint64_t) * y.nchunks * (NS * NS + NS) * slots);
   y.zero_end = off;
   y.dapart = off;
   if (op == PARARNN_OP_ADJOINT && with_da) off = round_up(off + sizeof(float) * y.nchunks * B * G * D);
@@ -273,21 +274,15 @@ int solve(int cell, const void* u, const float* a, const float* c0, const float*
     rc = record(o, k + 1, stream);
     if (rc) return rc;
     if (o->early_exit) {  // the next launch decides from this launch's row maxima
-      hipLaunchKernelGGL(rowmax_kernel, dim3(o->B, 1), dim3(256), 0, stream, ia.pmax, ia.maxupd, o->B,
-                         y.ntiles_d, y.nchunks, k - 1);
+      hipLaunchKernelGGL(rowmax_kernel, dim3(o->B), dim3(256), 0, stream, ia.pmax, ia.maxupd, o->B, y.ntiles_d,
+                         y.nchunks, k - 1);
       rc = check_hip(hipGetLastError());
       if (rc) return rc;
     }
   }
-  if (!o->early_exit) {
-    hipLaunchKernelGGL(rowmax_kernel, dim3(o->B, K), dim3(256), 0, stream, ia.pmax, ia.maxupd, o->B, y.ntiles_d,
-                       y.nchunks, 0);
-    rc = check_hip(hipGetLastError());
-    if (rc) return rc;
-  }
-  hipLaunchKernelGGL(newton_flags_kernel, dim3(1), dim3(256), 0, stream,
-                     static_cast<const unsigned int*>(ia.maxupd), o->B, K, o->tol, o->early_exit, iters,
-                     converged, max_update);
+  hipLaunchKernelGGL(newton_finalize_kernel, dim3(o->B, K), dim3(256), 0, stream,
+                     static_cast<const unsigned int*>(ia.pmax), ia.maxupd, o->B, y.ntiles_d, y.nchunks, K, o->tol,
+                     o->early_exit, iters, converged, max_update);
   return check_hip(hipGetLastError());
 }
 
