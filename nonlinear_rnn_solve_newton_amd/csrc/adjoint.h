@@ -35,8 +35,8 @@ struct AdjArgs {
   int B, L, D, nchunks, ntiles_d;
 };
 
-template <class Cell, class UT, int C, int T, int W, int LL>
-__global__ void __launch_bounds__(64 * W) adjoint_kernel(const AdjArgs p) {
+template <class Cell, class UT, int C, int T, int W, int LL, int OCC>
+__global__ void __launch_bounds__(64 * W, OCC) adjoint_kernel(const AdjArgs p) {
   constexpr int NS = Cell::NS, G = Cell::G;
   constexpr int LD = 64 / LL, CW = LD * C, CL = W * LL * T, NA = NS * NS + NS, NSEG = W * LL;
   constexpr uint32_t tag = 1u;

@@ -133,8 +133,8 @@ __device__ __forceinline__ void publish_incl(unsigned long long* incl, long long
     for (int c = 0; c < C; ++c) desc_put(incl + ((long long)chunk * NS + s) * BD + chan + c * cs, tag, x[s][c]);
 }
 
-template <class Cell, class UT, int C, int T, int W, int LL>
-__global__ void __launch_bounds__(64 * W) newton_iter_kernel(const IterArgs p) {
+template <class Cell, class UT, int C, int T, int W, int LL, int OCC>
+__global__ void __launch_bounds__(64 * W, OCC) newton_iter_kernel(const IterArgs p) {
   constexpr int NS = Cell::NS, G = Cell::G;
   constexpr int LD = 64 / LL;   // lanes along D
   constexpr int CW = LD * C;    // channels per workgroup

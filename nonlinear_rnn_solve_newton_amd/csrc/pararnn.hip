@@ -15,20 +15,21 @@ namespace {
 
 // ---------------------------------------------------------------------------
 // Launch configurations. Per (cell, C, operation): T timesteps per lane, W
-// waves per workgroup, LL lane groups along L per wave; a workgroup covers
-// (64/LL)*C channels x W*LL*T timesteps (one chunk of the look-back). The
+// waves per workgroup, LL lane groups along L per wave, OCC the waves per SIMD
+// the register allocation must allow; a workgroup covers (64/LL)*C channels x
+// W*LL*T timesteps (one chunk of the look-back). The
 // LSTM keeps at most two channels per lane (six scan values per channel).
 template <class Cell, int C, bool ADJ>
 struct Cfg;
-template <> struct Cfg<GruCell, 4, false> { static constexpr int T = 8, W = 4, LL = 4; };
-template <> struct Cfg<GruCell, 2, false> { static constexpr int T = 8, W = 8, LL = 2; };
-template <> struct Cfg<GruCell, 1, false> { static constexpr int T = 16, W = 8, LL = 1; };
-template <> struct Cfg<LstmCell, 1, false> { static constexpr int T = 16, W = 4, LL = 2; };
-template <> struct Cfg<GruCell, 4, true> { static constexpr int T = 4, W = 8, LL = 4; };
-template <> struct Cfg<GruCell, 2, true> { static constexpr int T = 8, W = 4, LL = 4; };
-template <> struct Cfg<GruCell, 1, true> { static constexpr int T = 8, W = 8, LL = 2; };
-template <> struct Cfg<LstmCell, 2, true> { static constexpr int T = 16, W = 4, LL = 1; };
-template <> struct Cfg<LstmCell, 1, true> { static constexpr int T = 8, W = 8, LL = 2; };
+template <> struct Cfg<GruCell, 4, false> { static constexpr int T = 8, W = 4, LL = 4, OCC = 3; };
+template <> struct Cfg<GruCell, 2, false> { static constexpr int T = 8, W = 8, LL = 2, OCC = 2; };
+template <> struct Cfg<GruCell, 1, false> { static constexpr int T = 16, W = 8, LL = 1, OCC = 2; };
+template <> struct Cfg<LstmCell, 1, false> { static constexpr int T = 8, W = 8, LL = 2, OCC = 4; };
+template <> struct Cfg<GruCell, 4, true> { static constexpr int T = 4, W = 8, LL = 4, OCC = 2; };
+template <> struct Cfg<GruCell, 2, true> { static constexpr int T = 8, W = 4, LL = 4, OCC = 2; };
+template <> struct Cfg<GruCell, 1, true> { static constexpr int T = 8, W = 8, LL = 2, OCC = 2; };
+template <> struct Cfg<LstmCell, 2, true> { static constexpr int T = 16, W = 4, LL = 1, OCC = 1; };
+template <> struct Cfg<LstmCell, 1, true> { static constexpr int T = 8, W = 8, LL = 2, OCC = 2; };
 
 // widest channel group per lane: the LSTM Newton iteration runs one channel
 // per lane (its per-step 2x2 Jacobian, residual and previous iterate leave no
@@ -167,7 +168,7 @@ int launch_iter(const IterArgs& a, hipStream_t s) {
   using K = Cfg<Cell, C, false>;
   const unsigned grid = static_cast<unsigned>(a.B) * a.ntiles_d * static_cast<unsigned>(a.nchunks);
   const IterArgs& b = a;
-  hipLaunchKernelGGL((newton_iter_kernel<Cell, UT, C, K::T, K::W, K::LL>), dim3(grid), dim3(64 * K::W), 0,
+  hipLaunchKernelGGL((newton_iter_kernel<Cell, UT, C, K::T, K::W, K::LL, K::OCC>), dim3(grid), dim3(64 * K::W), 0,
                      s, b);
   return check_hip(hipGetLastError());
 }
@@ -193,7 +194,7 @@ int launch_adj(const AdjArgs& a, hipStream_t s) {
   using K = Cfg<Cell, C, true>;
   const unsigned grid = static_cast<unsigned>(a.B) * a.ntiles_d * static_cast<unsigned>(a.nchunks);
   const AdjArgs& b = a;
-  hipLaunchKernelGGL((adjoint_kernel<Cell, UT, C, K::T, K::W, K::LL>), dim3(grid), dim3(64 * K::W), 0, s, b);
+  hipLaunchKernelGGL((adjoint_kernel<Cell, UT, C, K::T, K::W, K::LL, K::OCC>), dim3(grid), dim3(64 * K::W), 0, s, b);
   return check_hip(hipGetLastError());
 }
 
