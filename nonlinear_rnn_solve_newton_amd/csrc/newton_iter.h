@@ -22,6 +22,8 @@
 // the gate inputs, the previous iterate and the new iterate.
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace pararnn {
@@ -211,6 +213,11 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_iter_kernel(const IterArgs
     return;
   }
 
+  // The tile body, instantiated for full tiles (every step and channel valid:
+  // no clamping or guards, uniform per-step address bases) and partial ones.
+  uint32_t mbits = 0u;
+  auto tile_body = [&](auto full_tag) {
+  constexpr bool FULL = decltype(full_tag)::value;
   // ---- a1: stream gate inputs and the previous iterate -------------------
   // Loads are unconditional: rows beyond L are clamped to the last row and
   // channel groups beyond D to the last group, so every address is inside the
@@ -240,18 +247,27 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_iter_kernel(const IterArgs
   URaw<UT, C> uu[T][G];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
-    const uint32_t rr = static_cast<uint32_t>(min(lt0 + t, lastrow));
+    // full tiles: the step offset is uniform (scalar base), the lane offset fixed
+    const uint32_t rr = FULL ? static_cast<uint32_t>(lt0 + t) : static_cast<uint32_t>(min(lt0 + t, lastrow));
+    const uint32_t lane_s = FULL ? soff : rr * sstep + static_cast<uint32_t>(dcl * sizeof(float));
+    const uint32_t lane_u = FULL ? uoff : rr * ustep + static_cast<uint32_t>(dcl * sizeof(UT));
+    const uint32_t step_s = FULL ? static_cast<uint32_t>(t) * sstep : 0u;
+    const uint32_t step_u = FULL ? static_cast<uint32_t>(t) * ustep : 0u;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      if (p.sin[s]) ld_f32_stream<C>(sptr_in(s, rr * sstep + static_cast<uint32_t>(dcl * sizeof(float))), so[t][s]);
-      else
+      if (p.sin[s]) {
+        const char* sb = reinterpret_cast<const char*>(p.sin[s]) + sdelta + step_s;
+        ld_f32_stream<C>(reinterpret_cast<const float*>(sb + lane_s), so[t][s]);
+      } else {
 #pragma unroll
         for (int c = 0; c < C; ++c) so[t][s][c] = 0.0f;
+      }
     }
 #pragma unroll
-    for (int g = 0; g < G; ++g)
-      uu[t][g].load(reinterpret_cast<const UT*>(
-          ubase + static_cast<uint32_t>(rr * ustep + g * gstep + static_cast<uint32_t>(dcl * sizeof(UT)))));
+    for (int g = 0; g < G; ++g) {
+      const char* ub = ubase + static_cast<uint32_t>(step_u + g * gstep);
+      uu[t][g].load(reinterpret_cast<const UT*>(ub + lane_u));
+    }
   }
 
   // ---- a2 + a3: residual and Jacobian per step; serial scan of the lane's T steps
@@ -367,7 +383,9 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_iter_kernel(const IterArgs
   }
   if constexpr (LL > 1) excl.apply(x);
 
-  uint32_t mbits = 0u;
+  // max |update| over the lane's valid steps; the NaN-propagating maximum keeps
+  // a NaN anywhere in the row visible
+  float mx = 0.0f;
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     const int l = l0 + t;
@@ -385,22 +403,29 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_iter_kernel(const IterArgs
     for (int r = 0; r < NS; ++r)
 #pragma unroll
       for (int c = 0; c < C; ++c) x[r][c] = y[r][c];
-    if (dv && l < p.L) {
+    if (FULL || (dv && l < p.L)) {
 #pragma unroll
       for (int r = 0; r < NS; ++r) {
         float o[C];
 #pragma unroll
         for (int c = 0; c < C; ++c) {
           o[c] = so[t][r][c] + x[r][c];
-          mbits = max(mbits, __float_as_uint(fabsf(x[r][c])));
+          mx = __builtin_elementwise_maximum(mx, fabsf(x[r][c]));
         }
-        st_f32<C>(sptr_out(r, soff + t * sstep), o);
+        char* sb = reinterpret_cast<char*>(p.sout[r]) + sdelta + (FULL ? static_cast<uint32_t>(t) * sstep : 0u);
+        st_f32<C>(reinterpret_cast<float*>(sb + (FULL ? soff : soff + static_cast<uint32_t>(t) * sstep)), o);
       }
     }
   }
-  // row max of |update|: wave reduction on the bit patterns (NaN ranks above +inf)
+  // row max of |update|: wave reduction (NaN-propagating)
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mbits = max(mbits, static_cast<uint32_t>(__shfl_xor(mbits, off, 64)));
+  for (int off = 32; off >= 1; off >>= 1) mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, off, 64));
+  mbits = __float_as_uint(mx);
+  };
+  const bool full = (chunk + 1) * CL <= p.L && dt0 + CW <= p.D;
+  if (full) tile_body(std::true_type{});
+  else tile_body(std::false_type{});
+
   // workgroup max, one plain store per workgroup (same-address atomics from
   // every wave would serialise at the device coherence point)
   if (lane == 0) s_wmax[wave] = mbits;

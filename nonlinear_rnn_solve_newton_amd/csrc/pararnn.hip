@@ -21,9 +21,8 @@ namespace {
 // LSTM keeps at most two channels per lane (six scan values per channel).
 template <class Cell, int C, bool ADJ>
 struct Cfg;
-template <> struct Cfg<GruCell, 4, false> { static constexpr int T = 8, W = 4, LL = 4, OCC = 3; };
-template <> struct Cfg<GruCell, 2, false> { static constexpr int T = 8, W = 8, LL = 2, OCC = 2; };
-template <> struct Cfg<GruCell, 1, false> { static constexpr int T = 16, W = 8, LL = 1, OCC = 2; };
+template <> struct Cfg<GruCell, 2, false> { static constexpr int T = 16, W = 4, LL = 2, OCC = 3; };
+template <> struct Cfg<GruCell, 1, false> { static constexpr int T = 32, W = 4, LL = 1, OCC = 3; };
 template <> struct Cfg<LstmCell, 1, false> { static constexpr int T = 8, W = 8, LL = 2, OCC = 4; };
 template <> struct Cfg<GruCell, 4, true> { static constexpr int T = 4, W = 8, LL = 4, OCC = 2; };
 template <> struct Cfg<GruCell, 2, true> { static constexpr int T = 8, W = 4, LL = 4, OCC = 2; };
@@ -31,10 +30,10 @@ template <> struct Cfg<GruCell, 1, true> { static constexpr int T = 8, W = 8, LL
 template <> struct Cfg<LstmCell, 2, true> { static constexpr int T = 16, W = 4, LL = 1, OCC = 1; };
 template <> struct Cfg<LstmCell, 1, true> { static constexpr int T = 8, W = 8, LL = 2, OCC = 2; };
 
-// widest channel group per lane: the LSTM Newton iteration runs one channel
-// per lane (its per-step 2x2 Jacobian, residual and previous iterate leave no
-// registers for more), the LSTM adjoint two
-template <class Cell, bool ADJ> constexpr int max_c() { return Cell::NS == 2 ? (ADJ ? 2 : 1) : 4; }
+// widest channel group per lane. Newton iteration: the GRU runs two channels
+// per lane, the LSTM one (its per-step 2x2 Jacobian, residual and previous
+// iterate leave no registers for more); adjoint: GRU four, LSTM two.
+template <class Cell, bool ADJ> constexpr int max_c() { return Cell::NS == 2 ? (ADJ ? 2 : 1) : (ADJ ? 4 : 2); }
 
 // workgroup footprint of one configuration: timesteps (one look-back chunk)
 // and channels
