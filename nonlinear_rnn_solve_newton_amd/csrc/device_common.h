@@ -73,6 +73,46 @@ __device__ __forceinline__ void st_f32(float* p, const float (&v)[C]) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// ---------------------------------------------------------------------------
+// Buffer-resource access: a 128-bit descriptor in scalar registers (base,
+// byte extent) plus a 32-bit per-lane offset and a 32-bit uniform offset.
+// Offsets at or past the extent read 0 and drop stores, which handles every
+// tail without branches. Descriptors here cover one batch row of a tensor.
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+constexpr int kBufCfg = 0x00020000;  // 32-bit data format, raw (unformatted) access
+constexpr int kBufNT = 2;            // nontemporal cache policy
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           kBufCfg);
+}
+
+template <int C>
+__device__ __forceinline__ void buf_ld_f32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, float (&v)[C]) {
+  if constexpr (C == 4) {
+    const i32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kBufNT);
+    v[0] = __int_as_float(x.x); v[1] = __int_as_float(x.y); v[2] = __int_as_float(x.z); v[3] = __int_as_float(x.w);
+  } else if constexpr (C == 2) {
+    const i32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kBufNT);
+    v[0] = __int_as_float(x.x); v[1] = __int_as_float(x.y);
+  } else {
+    v[0] = __int_as_float(static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kBufNT)));
+  }
+}
+
+template <int C>
+__device__ __forceinline__ void buf_st_f32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, const float (&v)[C]) {
+  if constexpr (C == 4) {
+    __builtin_amdgcn_raw_buffer_store_b128(i32x4{__float_as_int(v[0]), __float_as_int(v[1]), __float_as_int(v[2]),
+                                                 __float_as_int(v[3])}, r, voff, soff, 0);
+  } else if constexpr (C == 2) {
+    __builtin_amdgcn_raw_buffer_store_b64(i32x2{__float_as_int(v[0]), __float_as_int(v[1])}, r, voff, soff, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(__float_as_int(v[0])), r, voff, soff, 0);
+  }
+}
+
 // Raw gate-input registers: bf16 inputs stay packed (two per 32-bit
 // register) until the cell evaluation widens them, which halves the registers
 // held while the loads are in flight.
@@ -86,6 +126,9 @@ struct URaw<float, C> {
   __device__ __forceinline__ void zero() {
 #pragma unroll
     for (int c = 0; c < C; ++c) v[c] = 0.0f;
+  }
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    buf_ld_f32<C>(r, voff, soff, v);
   }
   __device__ __forceinline__ float get(int c) const { return v[c]; }
 };
@@ -103,6 +146,17 @@ struct URaw<bf16, C> {
       w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
     } else {
       w[0] = static_cast<uint32_t>(__builtin_nontemporal_load(&p->bits));
+    }
+  }
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    if constexpr (C == 4) {
+      const i32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kBufNT);
+      w[0] = static_cast<uint32_t>(x.x);
+      w[1] = static_cast<uint32_t>(x.y);
+    } else if constexpr (C == 2) {
+      w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kBufNT);
+    } else {
+      w[0] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, kBufNT));
     }
   }
   __device__ __forceinline__ void zero() {

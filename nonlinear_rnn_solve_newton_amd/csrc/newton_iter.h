@@ -175,61 +175,57 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_iter_kernel(const IterArgs
   const int l0 = chunk * CL + (wave * LL + ll) * T;
   const long long BD = static_cast<long long>(p.B) * p.ntiles_d * CW;  // descriptor slots per component
   const long long chan = static_cast<long long>(tile) * CW + ld;
-  // Addressing: workgroup-uniform 64-bit bases (scalar registers) plus 32-bit
-  // per-lane byte offsets; a timestep advances the state by D floats and the
-  // gate inputs by G*D elements.
+  // Addressing: one buffer resource per tensor covering this chunk's rows of
+  // batch row b (scalar registers, extent = the chunk's rows below L), a
+  // 32-bit lane offset that advances one row per step, and the gate offset as
+  // the uniform offset. Rows at or past L read 0 and drop stores; lanes past D
+  // get an offset beyond every extent. Steps past L follow every valid step of
+  // their channel in scan order, so their (J, r) never reach a stored value.
   const int dt0 = (tile - b * p.ntiles_d) * CW;
-  const long long wrow = static_cast<long long>(b) * p.L + static_cast<long long>(chunk) * CL;
-  const char* __restrict__ ubase =
-      reinterpret_cast<const char*>(p.u) + (wrow * G * p.D + dt0) * static_cast<long long>(sizeof(UT));
-  const long long sdelta = (wrow * p.D + dt0) * static_cast<long long>(sizeof(float));
   const int lt0 = (wave * LL + ll) * T;  // lane's first timestep within the chunk
+  const long long wrow = static_cast<long long>(b) * p.L + static_cast<long long>(chunk) * CL;
   const uint32_t ustep = static_cast<uint32_t>(G * p.D * sizeof(UT));
   const uint32_t gstep = static_cast<uint32_t>(p.D * sizeof(UT));
   const uint32_t sstep = static_cast<uint32_t>(p.D * sizeof(float));
-  const uint32_t uoff = static_cast<uint32_t>(lt0) * ustep + static_cast<uint32_t>(ld * C * sizeof(UT));
-  const uint32_t soff = static_cast<uint32_t>(lt0) * sstep + static_cast<uint32_t>(ld * C * sizeof(float));
-  auto sptr_in = [&](int s, uint32_t off) {
-    return reinterpret_cast<const float*>(reinterpret_cast<const char*>(p.sin[s]) + sdelta + off);
-  };
-  auto sptr_out = [&](int s, uint32_t off) {
-    return reinterpret_cast<float*>(reinterpret_cast<char*>(p.sout[s]) + sdelta + off);
-  };
+  const uint32_t rows = static_cast<uint32_t>(min(p.L - chunk * CL, CL));
+  constexpr uint32_t kOOB = 0x80000000u;  // extents stay below 2^31 bytes
+  const uint32_t vu0 = dv ? static_cast<uint32_t>(lt0) * ustep + static_cast<uint32_t>(d0 * sizeof(UT)) : kOOB;
+  const uint32_t vs0 = dv ? static_cast<uint32_t>(lt0) * sstep + static_cast<uint32_t>(d0 * sizeof(float)) : kOOB;
+  const __amdgpu_buffer_rsrc_t ru =
+      make_rsrc(reinterpret_cast<const char*>(p.u) + wrow * G * p.D * static_cast<long long>(sizeof(UT)), rows * ustep);
+  __amdgpu_buffer_rsrc_t rin[NS], rout[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    rin[s] = make_rsrc(p.sin[s] ? p.sin[s] + wrow * p.D : nullptr, p.sin[s] ? rows * sstep : 0u);
+    rout[s] = make_rsrc(p.sout[s] + wrow * p.D, rows * sstep);
+  }
 
   if (skip) {
     // early exit fired earlier: keep the converged iterate, moved to this launch's output
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      const int l = l0 + t;
-      if (dv && l < p.L) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          float v[C];
-          ld_f32<C>(sptr_in(s, soff + t * sstep), v);
-          st_f32<C>(sptr_out(s, soff + t * sstep), v);
-        }
+      for (int s = 0; s < NS; ++s) {
+        float v[C];
+        buf_ld_f32<C>(rin[s], vs0 + t * sstep, 0u, v);
+        buf_st_f32<C>(rout[s], vs0 + t * sstep, 0u, v);
       }
     }
     return;
   }
 
-  // The tile body, instantiated for full tiles (every step and channel valid:
-  // no clamping or guards, uniform per-step address bases) and partial ones.
+  // The tile body, instantiated for full tiles (every step and channel valid,
+  // so no step needs masking out of the update size) and partial ones.
   uint32_t mbits = 0u;
   auto tile_body = [&](auto full_tag) {
   constexpr bool FULL = decltype(full_tag)::value;
   // ---- a1: stream gate inputs and the previous iterate -------------------
-  // Loads are unconditional: rows beyond L are clamped to the last row and
-  // channel groups beyond D to the last group, so every address is inside the
-  // tensors. Such steps only follow every valid step of their channel in scan
-  // order, so their (J, r) never reach a stored value.
-  const int lastrow = p.L - 1 - chunk * CL;                // >= 0: the chunk holds a valid row
-  const int dcl = (dv ? d0 : p.D - C) - dt0;               // >= 0: the tile holds a valid group
-  const int dc = dt0 + dcl;                                // clamped channel
+  const int dc = dv ? d0 : p.D - C;  // channel group for the per-channel loads
   float av[G][C];
 #pragma unroll
   for (int g = 0; g < G; ++g) ld_f32<C>(p.a + static_cast<long long>(g) * p.D + dc, av[g]);
   float sp[NS][C];  // iterate k-1 at l0 - 1 (the initial state at l0 == 0)
+  const int lastrow = p.L - 1 - chunk * CL;  // >= 0: the chunk holds a valid row
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     float v0[C], v1[C];
@@ -237,7 +233,7 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_iter_kernel(const IterArgs
     for (int c = 0; c < C; ++c) v0[c] = v1[c] = 0.0f;
     if (p.s0[s]) ld_f32<C>(p.s0[s] + static_cast<long long>(b) * p.D + dc, v0);
     if (p.sin[s]) {
-      const long long prow = wrow + min(max(lt0 - 1, -chunk * CL), lastrow);  // >= 0
+      const long long prow = wrow + min(max(lt0 - 1, -chunk * CL), lastrow);  // a row of batch b
       ld_f32<C>(p.sin[s] + prow * p.D + dc, v1);
     }
 #pragma unroll
@@ -247,27 +243,15 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_iter_kernel(const IterArgs
   URaw<UT, C> uu[T][G];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
-    // full tiles: the step offset is uniform (scalar base), the lane offset fixed
-    const uint32_t rr = FULL ? static_cast<uint32_t>(lt0 + t) : static_cast<uint32_t>(min(lt0 + t, lastrow));
-    const uint32_t lane_s = FULL ? soff : rr * sstep + static_cast<uint32_t>(dcl * sizeof(float));
-    const uint32_t lane_u = FULL ? uoff : rr * ustep + static_cast<uint32_t>(dcl * sizeof(UT));
-    const uint32_t step_s = FULL ? static_cast<uint32_t>(t) * sstep : 0u;
-    const uint32_t step_u = FULL ? static_cast<uint32_t>(t) * ustep : 0u;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      if (p.sin[s]) {
-        const char* sb = reinterpret_cast<const char*>(p.sin[s]) + sdelta + step_s;
-        ld_f32_stream<C>(reinterpret_cast<const float*>(sb + lane_s), so[t][s]);
-      } else {
+      if (p.sin[s]) buf_ld_f32<C>(rin[s], vs0 + t * sstep, 0u, so[t][s]);
+      else
 #pragma unroll
         for (int c = 0; c < C; ++c) so[t][s][c] = 0.0f;
-      }
     }
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const char* ub = ubase + static_cast<uint32_t>(step_u + g * gstep);
-      uu[t][g].load(reinterpret_cast<const UT*>(ub + lane_u));
-    }
+    for (int g = 0; g < G; ++g) uu[t][g].load(ru, vu0 + t * ustep, static_cast<uint32_t>(g) * gstep);
   }
 
   // ---- a2 + a3: residual and Jacobian per step; serial scan of the lane's T steps
@@ -403,18 +387,16 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_iter_kernel(const IterArgs
     for (int r = 0; r < NS; ++r)
 #pragma unroll
       for (int c = 0; c < C; ++c) x[r][c] = y[r][c];
-    if (FULL || (dv && l < p.L)) {
+    const bool valid = FULL || (dv && l < p.L);
 #pragma unroll
-      for (int r = 0; r < NS; ++r) {
-        float o[C];
+    for (int r = 0; r < NS; ++r) {
+      float o[C];
 #pragma unroll
-        for (int c = 0; c < C; ++c) {
-          o[c] = so[t][r][c] + x[r][c];
-          mx = __builtin_elementwise_maximum(mx, fabsf(x[r][c]));
-        }
-        char* sb = reinterpret_cast<char*>(p.sout[r]) + sdelta + (FULL ? static_cast<uint32_t>(t) * sstep : 0u);
-        st_f32<C>(reinterpret_cast<float*>(sb + (FULL ? soff : soff + static_cast<uint32_t>(t) * sstep)), o);
+      for (int c = 0; c < C; ++c) {
+        o[c] = so[t][r][c] + x[r][c];
+        if (valid) mx = __builtin_elementwise_maximum(mx, fabsf(x[r][c]));
       }
+      buf_st_f32<C>(rout[r], vs0 + t * sstep, 0u, o);  // dropped past L or D
     }
   }
   // row max of |update|: wave reduction (NaN-propagating)

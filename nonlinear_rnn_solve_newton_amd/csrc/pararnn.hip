@@ -221,7 +221,7 @@ int solve(int cell, const void* u, const float* a, const float* c0, const float*
   const int C = pick_c(cmax_for(cell, PARARNN_OP_SOLVE), o->D, usize, u, {a, h0, h, c0, c});
   if (!C || !aligned(u, usize)) return PARARNN_EUNSUPPORTED;
   const Geo g = geo_for(cell, PARARNN_OP_SOLVE, C);
-  // per-lane offsets inside one chunk of gate inputs are 32-bit
+  // one chunk of gate inputs (and of states) is addressed with 32-bit offsets below 2^31
   if (static_cast<double>(g.chunk) * ngates(cell) * o->D * 4.0 >= 2147483648.0) return PARARNN_EUNSUPPORTED;
   const Layout y = layout(cell, PARARNN_OP_SOLVE, o, false, g);
   if (ws_bytes < y.total) return PARARNN_EWORKSPACE;
