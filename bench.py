@@ -129,6 +129,25 @@ def traffic_from_counters(workload: str, fetch_csv: str, write_csv: str, iters: 
             "calibration": "1 GiB hipMemcpy device copy (__amd_rocclr_copyBuffer) in the same run"}
 
 
+def write_stats_summary(workload: str, stats_csv: str) -> str:
+    """profiles/<workload>_kernel_stats.md from rocprofv3 --kernel-trace --stats output."""
+    import csv
+
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = [f"# rocprofv3 kernel statistics: {workload}", "",
+             "Command (on the MI355X box, from /tmp with TMPDIR=/tmp):", "",
+             f"    rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o run -- "
+             f"python3 <repo>/bench.py --workload {workload} --steps 5 --warmup 2 --no-cpu-baseline", "",
+             f"Kernel sources digest: {source_digest()} (bench.py source_digest()).", "",
+             "| kernel | calls | average ns | min ns | max ns | % time |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| `{r['Name'][:100]}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | "
+                     f"{r['MaxNs']} | {float(r['Percentage']):.2f} |")
+    text = "\n".join(lines) + "\n"
+    (ROOT / "profiles" / f"{workload}_kernel_stats.md").write_text(text)
+    return text
+
+
 def cpu_baseline(w, x, iters, target_s=12.0):
     """fp64 oracle Newton solve on a channel sample of the same workload."""
     from nonlinear_rnn_solve_newton_amd.workloads import gather_channels, sample_channels
@@ -177,7 +196,15 @@ def main(argv=None):
                     help="also run a plain 1 GiB device copy (counter calibration for profiling)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/newton_iter_<workload>_traffic.json from rocprofv3 counter CSVs")
+    ap.add_argument("--stats-summary", metavar="KERNEL_STATS_CSV",
+                    help="write profiles/<workload>_kernel_stats.md from a rocprofv3 --stats CSV")
     args = ap.parse_args(argv)
+    if args.stats_summary:
+        sys.path.insert(0, str(ROOT))
+        from nonlinear_rnn_solve_newton_amd.workloads import HEADLINE, WORKLOADS
+        w = WORKLOADS[args.workload or HEADLINE]
+        print(write_stats_summary(w.name, args.stats_summary))
+        return 0
     if args.traffic_from:
         sys.path.insert(0, str(ROOT))
         from nonlinear_rnn_solve_newton_amd.workloads import HEADLINE, WORKLOADS
