@@ -194,6 +194,21 @@ struct GruCell {
     J[0][0] = fmaf(gc * a[2], drh, fmaf(gz, a[0], omz));
   }
 
+  // step() at the zero state h = 0, with the products of the zero state
+  // dropped: equal to step(a, u, {0}) bit for bit when every a is finite
+  // (a * 0 is then a signed zero that the following add absorbs).
+  __device__ static __forceinline__ void step_zero(const float (&a)[G], const float (&u)[G],
+                                                   float (&f)[NS], float (&J)[NS][NS]) {
+    const float z = sigm(u[0]);
+    const float r = sigm(u[1]);
+    const float c = tanh_fast(u[2]);
+    f[0] = z * c;
+    const float omz = 1.0f - z;
+    const float gz = c * z * omz;
+    const float gc = z * fmaf(-c, c, 1.0f);
+    J[0][0] = fmaf(gc * a[2], r, fmaf(gz, a[0], omz));
+  }
+
   __device__ static __forceinline__ void step_adj(const float (&a)[G], const float (&u)[G],
                                                   const float (&s)[NS], float (&J)[NS][NS],
                                                   float (&dfdu)[NS][G], float (&m)[G]) {
@@ -240,6 +255,29 @@ struct LstmCell {
     const float q = go * fmaf(-t, t, 1.0f);  // dh'/dc'
     const float dho = t * (go - go * go);
     const float X = fmaf(dci, a[0], fmaf(dcf, a[1], dcg * a[3]));  // dc'/dh
+    J[0][0] = gf;
+    J[0][1] = X;
+    J[1][0] = q * gf;
+    J[1][1] = fmaf(dho, a[2], q * X);
+  }
+
+  // step() at the zero state (c, h) = 0, with the products of the zero state
+  // dropped: equal to step(a, u, {0, 0}) bit for bit when every a is finite.
+  __device__ static __forceinline__ void step_zero(const float (&a)[G], const float (&u)[G],
+                                                   float (&f)[NS], float (&J)[NS][NS]) {
+    const float gi = sigm(u[0]);
+    const float gf = sigm(u[1]);
+    const float go = sigm(u[2]);
+    const float gg = tanh_fast(u[3]);
+    const float cn = gi * gg;
+    const float t = tanh_fast(cn);
+    f[0] = cn;
+    f[1] = go * t;
+    const float dci = gg * (gi - gi * gi);
+    const float dcg = gi * fmaf(-gg, gg, 1.0f);
+    const float q = go * fmaf(-t, t, 1.0f);
+    const float dho = t * (go - go * go);
+    const float X = fmaf(dci, a[0], dcg * a[3]);
     J[0][0] = gf;
     J[0][1] = X;
     J[1][0] = q * gf;

@@ -38,7 +38,7 @@ struct IterArgs {
   unsigned long long* agg;   // [nchunks][NS*NS+NS][B*D] chunk transforms
   unsigned int* ctr;      // [0,K) tickets
   unsigned int* maxupd;   // [K][B] fp32 bits of max |update| (reduced from pmax)
-  unsigned int* pmax;     // [K][grid] per-workgroup max |update| bits, indexed by ticket
+  unsigned int* pmax;     // [K][B][nchunks][ntiles_d] per-workgroup max |update| bits
   int B, L, D, k, K, nchunks, ntiles_d, early_exit;
   float tol;
 };
@@ -135,7 +135,9 @@ __device__ __forceinline__ void publish_incl(unsigned long long* incl, long long
     for (int c = 0; c < C; ++c) desc_put(incl + ((long long)chunk * NS + s) * BD + chan + c * cs, tag, x[s][c]);
 }
 
-template <class Cell, class UT, int C, int T, int W, int LL, int OCC>
+// FIRST: the launch of iteration 1, whose previous iterate is zero at every
+// step (no state input); only the initial state s0 enters, at l = 0.
+template <class Cell, class UT, int C, int T, int W, int LL, int OCC, bool FIRST>
 __global__ void __launch_bounds__(64 * W, OCC) newton_iter_kernel(const IterArgs p) {
   constexpr int NS = Cell::NS, G = Cell::G;
   constexpr int LD = 64 / LL;   // lanes along D
@@ -156,7 +158,7 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_iter_kernel(const IterArgs
   if (tid == 0) s_ticket = atomicAdd(p.ctr + (p.k - 1), 1u);
   __syncthreads();
   bool skip = false;
-  if (p.early_exit && p.k > 1) {
+  if (!FIRST && p.early_exit && p.k > 1) {
     // early exit: once every row's update of the previous launch is within tol
     // (skipped launches leave their row maxima at 0), this launch only carries
     // the iterate forward. The previous launch finished before this one began.
@@ -232,7 +234,7 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_iter_kernel(const IterArgs
 #pragma unroll
     for (int c = 0; c < C; ++c) v0[c] = v1[c] = 0.0f;
     if (p.s0[s]) ld_f32<C>(p.s0[s] + static_cast<long long>(b) * p.D + dc, v0);
-    if (p.sin[s]) {
+    if (!FIRST && p.sin[s]) {
       const long long prow = wrow + min(max(lt0 - 1, -chunk * CL), lastrow);  // a row of batch b
       ld_f32<C>(p.sin[s] + prow * p.D + dc, v1);
     }
@@ -245,7 +247,7 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_iter_kernel(const IterArgs
   for (int t = 0; t < T; ++t) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      if (p.sin[s]) buf_ld_f32<C>(rin[s], vs0 + t * sstep, 0u, so[t][s]);
+      if (!FIRST && p.sin[s]) buf_ld_f32<C>(rin[s], vs0 + t * sstep, 0u, so[t][s]);
       else
 #pragma unroll
         for (int c = 0; c < C; ++c) so[t][s][c] = 0.0f;
@@ -267,7 +269,14 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_iter_kernel(const IterArgs
       for (int g = 0; g < G; ++g) { ac[g] = av[g][c]; uc[g] = uu[t][g].get(c); }
 #pragma unroll
       for (int s = 0; s < NS; ++s) pc[s] = (t == 0) ? sp[s][c] : so[t - 1][s][c];
-      Cell::step(ac, uc, pc, f, J);
+      // Iteration 1 linearises at the zero iterate: from the third step of a
+      // lane on the cell is evaluated in its reduced form at the zero state.
+      // The general form on the first two steps (the second of the sequence's
+      // first lane is the first at the zero state, its first reads s0) makes
+      // a non-finite coefficient poison the lane as in the general form
+      // (inf * 0 = NaN enters r_t, and the scan carries it to every later step).
+      if (FIRST && t > 1) Cell::step_zero(ac, uc, f, J);
+      else Cell::step(ac, uc, pc, f, J);
 #pragma unroll
       for (int r = 0; r < NS; ++r) {
 #pragma unroll
@@ -393,7 +402,7 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_iter_kernel(const IterArgs
       float o[C];
 #pragma unroll
       for (int c = 0; c < C; ++c) {
-        o[c] = so[t][r][c] + x[r][c];
+        o[c] = FIRST ? x[r][c] : so[t][r][c] + x[r][c];
         if (valid) mx = __builtin_elementwise_maximum(mx, fabsf(x[r][c]));
       }
       buf_st_f32<C>(rout[r], vs0 + t * sstep, 0u, o);  // dropped past L or D
@@ -416,23 +425,33 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_iter_kernel(const IterArgs
     uint32_t m = s_wmax[0];
 #pragma unroll
     for (int w = 1; w < W; ++w) m = max(m, s_wmax[w]);
-    p.pmax[static_cast<long long>(p.k - 1) * gridDim.x + ticket] = m;
+    // partials of one row are contiguous: [k][b][chunk][channel tile]
+    p.pmax[((static_cast<long long>(p.k - 1) * p.B + b) * p.nchunks + chunk) * p.ntiles_d + (dt0 / CW)] = m;
   }
 }
 
+constexpr int kRowmaxThreads = 1024;  // block size of the row-max reductions
+
 // Row max of the per-workgroup partials of iteration k for batch row b (whole
-// block participates; result valid in thread 0). Workgroup ticket t covers
-// chunk t / (B * ntiles_d) and tile t % (B * ntiles_d), whose row is tile / ntiles_d.
+// block participates; result valid in every thread). A row's partials are
+// contiguous: n = nchunks * ntiles_d values.
 __device__ __forceinline__ uint32_t block_rowmax(const unsigned int* pmax, int B, int ntiles_d, int nchunks,
                                                  int k, int b, uint32_t* s_red) {
-  const long long nwg = static_cast<long long>(B) * ntiles_d * nchunks;
-  const int per_row = ntiles_d * nchunks;
+  const long long n = static_cast<long long>(nchunks) * ntiles_d;
+  const unsigned int* row = pmax + (static_cast<long long>(k) * B + b) * n;
+  // few blocks (one per row and iteration) read many partials: keep eight
+  // independent loads in flight per thread
+  constexpr int U = 8;
   uint32_t m = 0u;
-  for (int i = threadIdx.x; i < per_row; i += blockDim.x) {
-    const int chunk = i / ntiles_d, dt = i - chunk * ntiles_d;
-    const long long t = static_cast<long long>(chunk) * B * ntiles_d + static_cast<long long>(b) * ntiles_d + dt;
-    m = max(m, pmax[static_cast<long long>(k) * nwg + t]);
+  long long i = threadIdx.x;
+  for (; i + (U - 1) * static_cast<long long>(blockDim.x) < n; i += U * static_cast<long long>(blockDim.x)) {
+    uint32_t v[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) v[j] = row[i + j * static_cast<long long>(blockDim.x)];
+#pragma unroll
+    for (int j = 0; j < U; ++j) m = max(m, v[j]);
   }
+  for (; i < n; i += blockDim.x) m = max(m, row[i]);
   s_red[threadIdx.x] = m;
   __syncthreads();
   for (int off = blockDim.x / 2; off > 0; off >>= 1) {
@@ -445,9 +464,9 @@ __device__ __forceinline__ uint32_t block_rowmax(const unsigned int* pmax, int B
 }
 
 // Early-exit mode only: row maxima of iteration k, read by the next launch.
-__global__ void __launch_bounds__(256) rowmax_kernel(const unsigned int* pmax, unsigned int* maxupd, int B,
+__global__ void __launch_bounds__(kRowmaxThreads) rowmax_kernel(const unsigned int* pmax, unsigned int* maxupd, int B,
                                                      int ntiles_d, int nchunks, int k) {
-  __shared__ uint32_t s_red[256];
+  __shared__ uint32_t s_red[kRowmaxThreads];
   const uint32_t m = block_rowmax(pmax, B, ntiles_d, nchunks, k, blockIdx.x, s_red);
   if (threadIdx.x == 0) maxupd[static_cast<long long>(k) * B + blockIdx.x] = m;
 }
@@ -456,11 +475,11 @@ __global__ void __launch_bounds__(256) rowmax_kernel(const unsigned int* pmax, u
 // row maximum of iteration k (unless early exit already reduced it), copied
 // out as a float; the last iteration's blocks also write the row's
 // convergence flag, and block (0, K-1) the iteration count.
-__global__ void __launch_bounds__(256) newton_finalize_kernel(const unsigned int* pmax, unsigned int* maxupd,
+__global__ void __launch_bounds__(kRowmaxThreads) newton_finalize_kernel(const unsigned int* pmax, unsigned int* maxupd,
                                                               int B, int ntiles_d, int nchunks, int K, float tol,
                                                               int early_exit, int32_t* iters_out,
                                                               int32_t* conv_out, float* maxupd_out) {
-  __shared__ uint32_t s_red[256];
+  __shared__ uint32_t s_red[kRowmaxThreads];
   const int b = blockIdx.x, k = blockIdx.y, tid = threadIdx.x;
   uint32_t m;
   if (!early_exit) {

@@ -23,7 +23,7 @@ template <class Cell, int C, bool ADJ>
 struct Cfg;
 template <> struct Cfg<GruCell, 2, false> { static constexpr int T = 16, W = 4, LL = 2, OCC = 3; };
 template <> struct Cfg<GruCell, 1, false> { static constexpr int T = 32, W = 4, LL = 1, OCC = 3; };
-template <> struct Cfg<LstmCell, 1, false> { static constexpr int T = 8, W = 8, LL = 2, OCC = 4; };
+template <> struct Cfg<LstmCell, 1, false> { static constexpr int T = 24, W = 4, LL = 1, OCC = 2; };
 template <> struct Cfg<GruCell, 4, true> { static constexpr int T = 4, W = 8, LL = 4, OCC = 2; };
 template <> struct Cfg<GruCell, 2, true> { static constexpr int T = 8, W = 4, LL = 4, OCC = 2; };
 template <> struct Cfg<GruCell, 1, true> { static constexpr int T = 8, W = 8, LL = 2, OCC = 2; };
@@ -167,8 +167,12 @@ int launch_iter(const IterArgs& a, hipStream_t s) {
   using K = Cfg<Cell, C, false>;
   const unsigned grid = static_cast<unsigned>(a.B) * a.ntiles_d * static_cast<unsigned>(a.nchunks);
   const IterArgs& b = a;
-  hipLaunchKernelGGL((newton_iter_kernel<Cell, UT, C, K::T, K::W, K::LL, K::OCC>), dim3(grid), dim3(64 * K::W), 0,
-                     s, b);
+  if (a.k == 1)  // iteration 1 starts from the zero iterate and reads no state
+    hipLaunchKernelGGL((newton_iter_kernel<Cell, UT, C, K::T, K::W, K::LL, K::OCC, true>), dim3(grid),
+                       dim3(64 * K::W), 0, s, b);
+  else
+    hipLaunchKernelGGL((newton_iter_kernel<Cell, UT, C, K::T, K::W, K::LL, K::OCC, false>), dim3(grid),
+                       dim3(64 * K::W), 0, s, b);
   return check_hip(hipGetLastError());
 }
 
@@ -274,13 +278,13 @@ int solve(int cell, const void* u, const float* a, const float* c0, const float*
     rc = record(o, k + 1, stream);
     if (rc) return rc;
     if (o->early_exit) {  // the next launch decides from this launch's row maxima
-      hipLaunchKernelGGL(rowmax_kernel, dim3(o->B), dim3(256), 0, stream, ia.pmax, ia.maxupd, o->B, y.ntiles_d,
+      hipLaunchKernelGGL(rowmax_kernel, dim3(o->B), dim3(kRowmaxThreads), 0, stream, ia.pmax, ia.maxupd, o->B, y.ntiles_d,
                          y.nchunks, k - 1);
       rc = check_hip(hipGetLastError());
       if (rc) return rc;
     }
   }
-  hipLaunchKernelGGL(newton_finalize_kernel, dim3(o->B, K), dim3(256), 0, stream,
+  hipLaunchKernelGGL(newton_finalize_kernel, dim3(o->B, K), dim3(kRowmaxThreads), 0, stream,
                      static_cast<const unsigned int*>(ia.pmax), ia.maxupd, o->B, y.ntiles_d, y.nchunks, K, o->tol,
                      o->early_exit, iters, converged, max_update);
   return check_hip(hipGetLastError());

@@ -23,11 +23,12 @@ def dev():
     return torch.device("cuda:0")
 
 
-def gpu_solve(cell, x, iters=3, s0=None, tol=1e-4, early_exit=False, u=None):
-    """Run the HIP solve on the inputs of x; returns (states [NS][B][L][D] fp64, iters, conv, max_update)."""
+def gpu_solve(cell, x, iters=3, s0=None, tol=1e-4, early_exit=False, u=None, a=None):
+    """Run the HIP solve on the inputs of x (u or a replaced when given); returns
+    (states [NS][B][L][D] fp64, iters, conv, max_update)."""
     d = dev()
     ug = (x.u if u is None else u).to(d)
-    ag = x.a.to(d)
+    ag = (x.a if a is None else a).to(d)
     kw = {}
     if s0 is not None:
         s0t = torch.as_tensor(s0, dtype=torch.float32)

@@ -118,6 +118,32 @@ def test_nan_input_propagates():
 
 
 @pytest.mark.parametrize("cell", ["gru", "lstm"])
+@pytest.mark.parametrize("with_s0", [False, True], ids=["s0_zero", "s0_given"])
+def test_nonfinite_coefficient_propagates(cell, with_s0):
+    """Non-finite coefficients (inf in one channel, NaN in another) give the
+    oracle's NaN pattern: a * 0 at the zero starting iterate is NaN, so the
+    channel turns NaN from its first step at that iterate on, while the first
+    step from a given s0 may stay finite. The GPU's first iteration evaluates
+    most steps in a reduced form at the zero state; the other channels, also
+    those of the same workgroup, keep their values."""
+    say(f"solve {cell} non-finite coefficients, s0 {'given' if with_s0 else 'zero'}")
+    B, L, D = 2, 700, 96
+    x = make_inputs(cell, B, L, D, seed=37, u_dtype="bf16")
+    a = x.a.clone()
+    a[1, 5] = float("inf")
+    a[2, 9] = float("nan")
+    NS = 2 if cell == "lstm" else 1
+    s0 = np.random.default_rng(3).normal(size=(NS, B, D)).astype(np.float32) if with_s0 else None
+    S, iters, conv, mu = gpu_solve(cell, x, iters=3, a=a, s0=s0)
+    want, upd = O.newton(cell, x.u, a, K=3, s0=s0_float32(s0))
+    assert np.isnan(want[..., 1:, 5]).all() and np.isnan(want[..., 1:, 9]).all()
+    assert np.array_equal(np.isnan(S), np.isnan(want)), "NaN pattern differs from the oracle's"
+    fin = ~np.isnan(want)
+    assert np.abs(S[fin] - want[fin]).max() <= STATE_TOL
+    assert np.isnan(mu).all() and not conv.any() and iters == 3
+
+
+@pytest.mark.parametrize("cell", ["gru", "lstm"])
 def test_deterministic_and_workspace_reuse(cell):
     say(f"solve {cell} determinism")
     x = make_inputs(cell, 2, 3000, 256, seed=29, u_dtype="bf16")
