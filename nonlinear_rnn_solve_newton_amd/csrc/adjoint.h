@@ -59,82 +59,104 @@ __global__ void __launch_bounds__(64 * W, OCC) adjoint_kernel(const AdjArgs p) {
   const int chunk = p.nchunks - 1 - rchunk;  // chunks are taken from the end of L
   const int tile = static_cast<int>(ticket - static_cast<unsigned int>(rchunk) * ntiles);
   const int b = tile / p.ntiles_d;
-  const int d0 = (tile - b * p.ntiles_d) * CW + ld * C;
+  const int dt0 = (tile - b * p.ntiles_d) * CW;
+  const int d0 = dt0 + ld * C;
   const bool dv = d0 < p.D;
   const int q = wave * LL + ll;          // position in scan order (from the end)
-  const int l0 = chunk * CL + (NSEG - 1 - q) * T;
+  const int lt0 = (NSEG - 1 - q) * T;    // lane's first step within the chunk
+  const int l0 = chunk * CL + lt0;
   const long long BD = static_cast<long long>(p.B) * p.ntiles_d * CW;  // descriptor slots per component
   const long long chan = static_cast<long long>(tile) * CW + ld;
-  const long long row0 = static_cast<long long>(b) * p.L;
-  const UT* __restrict__ u = static_cast<const UT*>(p.u);
+  // Addressing as in the Newton iteration: per-chunk buffer resources over
+  // batch row b (u one row past the chunk, for the Jacobian of the step that
+  // follows the chunk), 32-bit lane offsets, rows at or past L read 0 and
+  // drop stores, lanes past D get an offset beyond every extent.
+  const long long wrow = static_cast<long long>(b) * p.L + static_cast<long long>(chunk) * CL;
+  const uint32_t ustep = static_cast<uint32_t>(G * p.D * sizeof(UT));
+  const uint32_t gstep = static_cast<uint32_t>(p.D * sizeof(UT));
+  const uint32_t sstep = static_cast<uint32_t>(p.D * sizeof(float));
+  const uint32_t dstep = static_cast<uint32_t>(G * p.D * sizeof(float));
+  const int crow = p.L - chunk * CL;  // rows from the chunk start to the end of L
+  const uint32_t rows = static_cast<uint32_t>(min(crow, CL));
+  const uint32_t rows_u = static_cast<uint32_t>(min(crow, CL + 1));
+  constexpr uint32_t kOOB = 0x80000000u;  // extents stay below 2^31 bytes
+  const uint32_t vu0 = dv ? static_cast<uint32_t>(lt0) * ustep + static_cast<uint32_t>(d0 * sizeof(UT)) : kOOB;
+  const uint32_t vs0 = dv ? static_cast<uint32_t>(lt0) * sstep + static_cast<uint32_t>(d0 * sizeof(float)) : kOOB;
+  const uint32_t vd0 = dv ? static_cast<uint32_t>(lt0) * dstep + static_cast<uint32_t>(d0 * sizeof(float)) : kOOB;
+  const __amdgpu_buffer_rsrc_t ru =
+      make_rsrc(reinterpret_cast<const char*>(p.u) + wrow * G * p.D * static_cast<long long>(sizeof(UT)), rows_u * ustep);
+  __amdgpu_buffer_rsrc_t rS[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) rS[s] = make_rsrc(p.S[s] + wrow * p.D, rows * sstep);
+  const __amdgpu_buffer_rsrc_t rdh = make_rsrc(p.dh + wrow * p.D, rows * sstep);
+  const __amdgpu_buffer_rsrc_t rdu = make_rsrc(p.du + wrow * G * p.D, rows * dstep);
 
+  float dacc[G][C];  // this lane's part of da
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int c = 0; c < C; ++c) dacc[g][c] = 0.0f;
+
+  // The tile body, instantiated for tiles whose steps (including the one after
+  // the chunk) all lie below L and whose channels all lie below D, and for
+  // the others, which mask the steps past L to identity transforms.
+  auto tile_body = [&](auto full_tag) {
+  constexpr bool FULL = decltype(full_tag)::value;
+  const int dc = dv ? d0 : p.D - C;  // channel group for the per-channel loads
   float av[G][C];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    if (dv) ld_f32<C>(p.a + static_cast<long long>(g) * p.D + d0, av[g]);
-    else
-#pragma unroll
-      for (int c = 0; c < C; ++c) av[g][c] = 0.0f;
-  }
-  // states S_{m-1} and inputs u_m for m = l0 .. l0 + T
+  for (int g = 0; g < G; ++g) ld_f32<C>(p.a + static_cast<long long>(g) * p.D + dc, av[g]);
+  // states S_{m-1} and inputs u_m for m = l0 .. l0 + T; S_{l0-1} is the
+  // initial state at l0 == 0 and otherwise the row before the lane (clamped
+  // into the sequence for lanes past L, whose steps are masked)
   float sv[T + 1][NS][C];
   URaw<UT, C> uu[T + 1][G];
   float gv[T][C];
 #pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    float v0[C], v1[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) v0[c] = 0.0f;
+    if (p.s0[s]) ld_f32<C>(p.s0[s] + static_cast<long long>(b) * p.D + dc, v0);
+    const long long prow = static_cast<long long>(b) * p.L + min(max(l0 - 1, 0), p.L - 1);
+    ld_f32<C>(p.S[s] + prow * p.D + dc, v1);
+#pragma unroll
+    for (int c = 0; c < C; ++c) sv[0][s][c] = (l0 == 0) ? v0[c] : v1[c];
+  }
+#pragma unroll
   for (int t = 0; t <= T; ++t) {
-    const int m = l0 + t;
-    const bool v = dv && m < p.L;
+    if (t > 0) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-#pragma unroll
-      for (int c = 0; c < C; ++c) sv[t][s][c] = 0.0f;
-      if (v) {
-        if (m == 0) {
-          if (p.s0[s]) ld_f32<C>(p.s0[s] + static_cast<long long>(b) * p.D + d0, sv[t][s]);
-        } else {
-          ld_f32<C>(p.S[s] + (row0 + m - 1) * p.D + d0, sv[t][s]);
-        }
-      }
+      for (int s = 0; s < NS; ++s) buf_ld_f32<C>(rS[s], vs0 + (t - 1) * sstep, 0u, sv[t][s]);
     }
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      if (v) uu[t][g].load(u + ((row0 + m) * G + g) * p.D + d0);
-      else uu[t][g].zero();
-    }
-    if (t < T) {
-      if (v) ld_f32<C>(p.dh + (row0 + m) * p.D + d0, gv[t]);
-      else
-#pragma unroll
-        for (int c = 0; c < C; ++c) gv[t][c] = 0.0f;
-    }
+    for (int g = 0; g < G; ++g) uu[t][g].load(ru, vu0 + t * ustep, static_cast<uint32_t>(g) * gstep);
+    if (t < T) buf_ld_f32<C>(rdh, vs0 + t * sstep, 0u, gv[t]);
   }
 
-  // cell evaluations at m = l0 + t: J_m for t = 0..T, dfdu_m and m_g for t < T
+  // cell evaluations at m = l0 + t: J_m for t = 0..T, the input-gradient
+  // coefficients for t < T
+  constexpr int NK = Cell::NK;
   float Jm[T + 1][NS][NS][C];
-  float dfdu[T][NS][G][C];
-  float mult[T][G][C];
+  float kc[T][NK][C];
 #pragma unroll
   for (int t = 0; t <= T; ++t) {
-    const bool v = dv && (l0 + t) < p.L;
+    const bool v = FULL || (dv && (l0 + t) < p.L);
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-      float ac[G], uc[G], sc[NS], J[NS][NS], du_[NS][G], mm[G];
+      float ac[G], uc[G], sc[NS], J[NS][NS], kk[NK];
 #pragma unroll
       for (int g = 0; g < G; ++g) { ac[g] = av[g][c]; uc[g] = uu[t][g].get(c); }
 #pragma unroll
       for (int s = 0; s < NS; ++s) sc[s] = sv[t][s][c];
-      Cell::step_adj(ac, uc, sc, J, du_, mm);
+      Cell::step_adj(ac, uc, sc, J, kk);
 #pragma unroll
       for (int r = 0; r < NS; ++r)
 #pragma unroll
         for (int s = 0; s < NS; ++s) Jm[t][r][s][c] = v ? J[r][s] : (r == s ? 1.0f : 0.0f);
       if (t < T) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-#pragma unroll
-          for (int r = 0; r < NS; ++r) dfdu[t][r][g][c] = du_[r][g];
-          mult[t][g][c] = mm[g];
-        }
+        for (int i = 0; i < NK; ++i) kc[t][i][c] = kk[i];
       }
     }
   }
@@ -243,11 +265,6 @@ __global__ void __launch_bounds__(64 * W, OCC) adjoint_kernel(const AdjArgs p) {
   }
   if constexpr (LL > 1) excl.apply(lam);
 
-  float dacc[G][C];
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int c = 0; c < C; ++c) dacc[g][c] = 0.0f;
 #pragma unroll
   for (int t = T - 1; t >= 0; --t) {
     const int l = l0 + t;
@@ -265,36 +282,44 @@ __global__ void __launch_bounds__(64 * W, OCC) adjoint_kernel(const AdjArgs p) {
     for (int r = 0; r < NS; ++r)
 #pragma unroll
       for (int c = 0; c < C; ++c) lam[r][c] = y[r][c];
-    if (dv && l < p.L) {
+    const bool valid = FULL || (dv && l < p.L);
+    float o[G][C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      float kk[NK], sc[NS], lc[NS], du_[G], mm[G];
+#pragma unroll
+      for (int i = 0; i < NK; ++i) kk[i] = kc[t][i][c];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) { sc[s] = sv[t][s][c]; lc[s] = lam[s][c]; }
+      Cell::grad_u(kk, sc, lc, du_, mm);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
+        o[g][c] = du_[g];
+        if (valid) dacc[g][c] = fmaf(mm[g], du_[g], dacc[g][c]);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      buf_st_f32<C, kBufNT>(rdu, vd0 + t * dstep, static_cast<uint32_t>(g) * sstep, o[g]);  // dropped past L or D
+    if (l == 0 && dv && p.ds0) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
         float o[C];
 #pragma unroll
         for (int c = 0; c < C; ++c) {
           float a2 = 0.0f;
 #pragma unroll
-          for (int r = 0; r < NS; ++r) a2 = fmaf(dfdu[t][r][g][c], lam[r][c], a2);
+          for (int r = 0; r < NS; ++r) a2 = fmaf(Jm[0][r][s][c], lam[r][c], a2);
           o[c] = a2;
-          dacc[g][c] = fmaf(mult[t][g][c], a2, dacc[g][c]);
         }
-        st_f32<C>(p.du + ((row0 + l) * G + g) * p.D + d0, o);
-      }
-      if (l == 0 && p.ds0) {
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          float o[C];
-#pragma unroll
-          for (int c = 0; c < C; ++c) {
-            float a2 = 0.0f;
-#pragma unroll
-            for (int r = 0; r < NS; ++r) a2 = fmaf(Jm[0][r][s][c], lam[r][c], a2);
-            o[c] = a2;
-          }
-          st_f32<C>(p.ds0 + (static_cast<long long>(s) * p.B + b) * p.D + d0, o);
-        }
+        st_f32<C>(p.ds0 + (static_cast<long long>(s) * p.B + b) * p.D + d0, o);
       }
     }
   }
+  };
+  const bool full = (chunk + 1) * CL < p.L && dt0 + CW <= p.D;
+  if (full) tile_body(std::true_type{});
+  else tile_body(std::false_type{});
 
   if (p.da_part) {
     // per-workgroup partial of da, summed in a fixed order: lane groups via

@@ -101,15 +101,16 @@ __device__ __forceinline__ void buf_ld_f32(__amdgpu_buffer_rsrc_t r, uint32_t vo
   }
 }
 
-template <int C>
+// AUX: cache policy of the store (0 default, kBufNT for data not read again soon)
+template <int C, int AUX = 0>
 __device__ __forceinline__ void buf_st_f32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, const float (&v)[C]) {
   if constexpr (C == 4) {
     __builtin_amdgcn_raw_buffer_store_b128(i32x4{__float_as_int(v[0]), __float_as_int(v[1]), __float_as_int(v[2]),
-                                                 __float_as_int(v[3])}, r, voff, soff, 0);
+                                                 __float_as_int(v[3])}, r, voff, soff, AUX);
   } else if constexpr (C == 2) {
-    __builtin_amdgcn_raw_buffer_store_b64(i32x2{__float_as_int(v[0]), __float_as_int(v[1])}, r, voff, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(i32x2{__float_as_int(v[0]), __float_as_int(v[1])}, r, voff, soff, AUX);
   } else {
-    __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(__float_as_int(v[0])), r, voff, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(__float_as_int(v[0])), r, voff, soff, AUX);
   }
 }
 
@@ -170,8 +171,11 @@ struct URaw<bf16, C> {
 
 // ---------------------------------------------------------------------------
 // Cells. step() evaluates the next state f and its Jacobian J = df/ds at the
-// previous state s; step_adj() also returns dfdu = df/du and the multiplier
-// m of each coefficient in its gate pre-activation (df/da_g = dfdu[.][g] * m_g).
+// previous state s. step_adj() returns J and NK coefficients k from which
+// grad_u() forms, for an adjoint lambda, the input gradient
+// du_g = sum_r lambda_r df_r/du_g and the multiplier m_g of a_g in gate g's
+// pre-activation (dL/da_g = du_g * m_g); k is the compact form of df/du the
+// reverse scan keeps per step.
 // ParaGRU: diagonal Jacobian (1x1 per channel); ParaLSTM: 2x2 over (c, h),
 // per the ParaRNN article's section "Engenharia pra escalar".
 struct GruCell {
@@ -209,9 +213,9 @@ struct GruCell {
     J[0][0] = fmaf(gc * a[2], r, fmaf(gz, a[0], omz));
   }
 
+  static constexpr int NK = 4;  // dh'/du_z, dh'/du_r, dh'/du_c, r h
   __device__ static __forceinline__ void step_adj(const float (&a)[G], const float (&u)[G],
-                                                  const float (&s)[NS], float (&J)[NS][NS],
-                                                  float (&dfdu)[NS][G], float (&m)[G]) {
+                                                  const float (&s)[NS], float (&J)[NS][NS], float (&k)[NK]) {
     const float h = s[0];
     const float z = sigm(fmaf(a[0], h, u[0]));
     const float r = sigm(fmaf(a[1], h, u[1]));
@@ -224,13 +228,22 @@ struct GruCell {
     const float rr = r - r * r;
     const float drh = fmaf(h * a[1], rr, r);
     J[0][0] = fmaf(gc * a[2], drh, fmaf(gz, a[0], omz));
-    dfdu[0][0] = gz;
-    dfdu[0][1] = gc * a[2] * h * rr;
-    dfdu[0][2] = gc;
-    m[0] = h;
-    m[1] = h;
-    m[2] = rh;
+    k[0] = gz;
+    k[1] = gc * a[2] * h * rr;
+    k[2] = gc;
+    k[3] = rh;
   }
+
+  __device__ static __forceinline__ void grad_u(const float (&k)[NK], const float (&s)[NS], const float (&lam)[NS],
+                                                float (&du)[G], float (&m)[G]) {
+    du[0] = k[0] * lam[0];
+    du[1] = k[1] * lam[0];
+    du[2] = k[2] * lam[0];
+    m[0] = s[0];
+    m[1] = s[0];
+    m[2] = k[3];
+  }
+
 };
 
 struct LstmCell {
@@ -284,9 +297,12 @@ struct LstmCell {
     J[1][1] = fmaf(dho, a[2], q * X);
   }
 
+  // q = dh'/dc', then dc'/du_i, dc'/du_f, dc'/du_g and dh'/du_o; the input
+  // gates reach h' only through c' (dh'/du_x = q dc'/du_x), and every gate
+  // pre-activation multiplies its coefficient by h.
+  static constexpr int NK = 5;
   __device__ static __forceinline__ void step_adj(const float (&a)[G], const float (&u)[G],
-                                                  const float (&s)[NS], float (&J)[NS][NS],
-                                                  float (&dfdu)[NS][G], float (&m)[G]) {
+                                                  const float (&s)[NS], float (&J)[NS][NS], float (&k)[NK]) {
     const float cp = s[0], hp = s[1];
     const float gi = sigm(fmaf(a[0], hp, u[0]));
     const float gf = sigm(fmaf(a[1], hp, u[1]));
@@ -304,10 +320,26 @@ struct LstmCell {
     J[0][1] = X;
     J[1][0] = q * gf;
     J[1][1] = fmaf(dho, a[2], q * X);
-    dfdu[0][0] = dci; dfdu[0][1] = dcf; dfdu[0][2] = 0.0f; dfdu[0][3] = dcg;
-    dfdu[1][0] = q * dci; dfdu[1][1] = q * dcf; dfdu[1][2] = dho; dfdu[1][3] = q * dcg;
-    m[0] = hp; m[1] = hp; m[2] = hp; m[3] = hp;
+    k[0] = q;
+    k[1] = dci;
+    k[2] = dcf;
+    k[3] = dcg;
+    k[4] = dho;
   }
+
+  __device__ static __forceinline__ void grad_u(const float (&k)[NK], const float (&s)[NS], const float (&lam)[NS],
+                                                float (&du)[G], float (&m)[G]) {
+    const float mu = fmaf(k[0], lam[1], lam[0]);  // total dL/dc' through c' and h'
+    du[0] = mu * k[1];
+    du[1] = mu * k[2];
+    du[2] = lam[1] * k[4];
+    du[3] = mu * k[3];
+    m[0] = s[1];
+    m[1] = s[1];
+    m[2] = s[1];
+    m[3] = s[1];
+  }
+
 };
 
 // ---------------------------------------------------------------------------

@@ -18,22 +18,26 @@ namespace {
 // waves per workgroup, LL lane groups along L per wave, OCC the waves per SIMD
 // the register allocation must allow; a workgroup covers (64/LL)*C channels x
 // W*LL*T timesteps (one chunk of the look-back). The
-// LSTM keeps at most two channels per lane (six scan values per channel).
+// LSTM keeps one channel per lane (six scan values per channel).
 template <class Cell, int C, bool ADJ>
 struct Cfg;
 template <> struct Cfg<GruCell, 2, false> { static constexpr int T = 16, W = 4, LL = 2, OCC = 3; };
 template <> struct Cfg<GruCell, 1, false> { static constexpr int T = 32, W = 4, LL = 1, OCC = 3; };
 template <> struct Cfg<LstmCell, 1, false> { static constexpr int T = 24, W = 4, LL = 1, OCC = 2; };
-template <> struct Cfg<GruCell, 4, true> { static constexpr int T = 4, W = 8, LL = 4, OCC = 2; };
-template <> struct Cfg<GruCell, 2, true> { static constexpr int T = 8, W = 4, LL = 4, OCC = 2; };
+template <> struct Cfg<GruCell, 2, true> { static constexpr int T = 8, W = 4, LL = 2, OCC = 3; };
 template <> struct Cfg<GruCell, 1, true> { static constexpr int T = 8, W = 8, LL = 2, OCC = 2; };
-template <> struct Cfg<LstmCell, 2, true> { static constexpr int T = 16, W = 4, LL = 1, OCC = 1; };
-template <> struct Cfg<LstmCell, 1, true> { static constexpr int T = 8, W = 8, LL = 2, OCC = 2; };
+template <> struct Cfg<LstmCell, 1, true> { static constexpr int T = 16, W = 4, LL = 1, OCC = 2; };
+// Iteration 1 (no state input, lighter cell form): same chunk length and
+// channel tile, its own split into waves and steps.
+template <class Cell, int C>
+struct CfgFirst : Cfg<Cell, C, false> {};
 
 // widest channel group per lane. Newton iteration: the GRU runs two channels
 // per lane, the LSTM one (its per-step 2x2 Jacobian, residual and previous
-// iterate leave no registers for more); adjoint: GRU four, LSTM two.
-template <class Cell, bool ADJ> constexpr int max_c() { return Cell::NS == 2 ? (ADJ ? 2 : 1) : (ADJ ? 4 : 2); }
+// iterate leave no registers for more); adjoint: GRU two, LSTM one (wider
+// groups either spill or need so few steps per lane that the per-lane scan
+// overhead outweighs the wider loads).
+template <class Cell, bool ADJ> constexpr int max_c() { return Cell::NS == 2 ? 1 : 2; }
 
 // workgroup footprint of one configuration: timesteps (one look-back chunk)
 // and channels
@@ -165,11 +169,14 @@ int clear_ws(char* ws, const Layout& y, float* user, long long nuser, hipStream_
 template <class Cell, class UT, int C>
 int launch_iter(const IterArgs& a, hipStream_t s) {
   using K = Cfg<Cell, C, false>;
+  using K1 = CfgFirst<Cell, C>;
+  static_assert(K1::W * K1::LL * K1::T == K::W * K::LL * K::T && K1::LL == K::LL,
+                "iteration 1 shares the chunk length and channel tile of the later iterations");
   const unsigned grid = static_cast<unsigned>(a.B) * a.ntiles_d * static_cast<unsigned>(a.nchunks);
   const IterArgs& b = a;
   if (a.k == 1)  // iteration 1 starts from the zero iterate and reads no state
-    hipLaunchKernelGGL((newton_iter_kernel<Cell, UT, C, K::T, K::W, K::LL, K::OCC, true>), dim3(grid),
-                       dim3(64 * K::W), 0, s, b);
+    hipLaunchKernelGGL((newton_iter_kernel<Cell, UT, C, K1::T, K1::W, K1::LL, K1::OCC, true>), dim3(grid),
+                       dim3(64 * K1::W), 0, s, b);
   else
     hipLaunchKernelGGL((newton_iter_kernel<Cell, UT, C, K::T, K::W, K::LL, K::OCC, false>), dim3(grid),
                        dim3(64 * K::W), 0, s, b);
@@ -206,7 +213,10 @@ int launch_adj_c(int C, const AdjArgs& a, hipStream_t s) {
   if constexpr (max_c<Cell, true>() >= 4) {
     if (C == 4) return launch_adj<Cell, UT, 4>(a, s);
   }
-  return C == 2 ? launch_adj<Cell, UT, 2>(a, s) : launch_adj<Cell, UT, 1>(a, s);
+  if constexpr (max_c<Cell, true>() >= 2) {
+    if (C == 2) return launch_adj<Cell, UT, 2>(a, s);
+  }
+  return launch_adj<Cell, UT, 1>(a, s);
 }
 
 template <class Cell>
@@ -332,7 +342,11 @@ extern "C" int32_t pararnn_adjoint(int32_t cell, const void* u, const float* a, 
   const int C = pick_c(cmax_for(cell, PARARNN_OP_ADJOINT), o->D, usize, u,
                       {a, h0, h, dh, du, ds0, da, lstm ? c0 : nullptr, lstm ? c : nullptr});
   if (!C || !aligned(u, usize)) return PARARNN_EUNSUPPORTED;
-  const Layout y = layout(cell, PARARNN_OP_ADJOINT, o, da != nullptr, geo_for(cell, PARARNN_OP_ADJOINT, C));
+  const Geo g = geo_for(cell, PARARNN_OP_ADJOINT, C);
+  // one chunk of gate inputs (plus the row after it) and of du is addressed
+  // with 32-bit offsets below 2^31
+  if ((g.chunk + 1.0) * ngates(cell) * o->D * 4.0 >= 2147483648.0) return PARARNN_EUNSUPPORTED;
+  const Layout y = layout(cell, PARARNN_OP_ADJOINT, o, da != nullptr, g);
   if (ws_bytes < y.total) return PARARNN_EWORKSPACE;
   if (!aligned(ws, kAlign)) return PARARNN_EUNSUPPORTED;
   char* w = static_cast<char*>(ws);
