@@ -44,7 +44,8 @@ def _bind(path):
     lib.oracle_newton.argtypes = [I, I, I, I, I, P, P, P, P, P, P, I]
     lib.oracle_adjoint.argtypes = [I, I, I, I, P, P, P, P, P, P, P, P, I]
     lib.oracle_cell.argtypes = [I, I, P, P, P, P, P, P, P]
-    for f in (lib.oracle_seq, lib.oracle_newton, lib.oracle_adjoint, lib.oracle_cell):
+    lib.oracle_scan.argtypes = [I, I, I, I, P, P, P, P, I]
+    for f in (lib.oracle_seq, lib.oracle_newton, lib.oracle_adjoint, lib.oracle_cell, lib.oracle_scan):
         f.restype = I
     return lib
 
@@ -190,6 +191,33 @@ def cell(cell_name, s, u, a):
     if rc:
         raise ValueError(f"oracle_cell failed ({rc})")
     return dict(f=f, J=J, dfdu=dfdu, dfda=dfda)
+
+
+def scan(A, b, s0=None, nthreads=None):
+    """Linear recurrence s_l = A_l s_{l-1} + b_l per channel, s_{-1} = s0.
+
+    ns = 1: A, b [B][L][D]; ns = 2: A [2][2][B][L][D] (block rows first), b
+    [2][B][L][D]; s0 [ns][B][D] or None. Returns s with the shape of b (fp64).
+    """
+    A = _np(A, np.float64)
+    b = _np(b, np.float64)
+    if A.ndim == 3:
+        ns, shape = 1, b.shape
+    elif A.ndim == 5 and A.shape[:2] == (2, 2):
+        ns, shape = 2, b.shape[1:]
+    else:
+        raise ValueError("A must be [B][L][D] or [2][2][B][L][D]")
+    if b.shape != ((shape) if ns == 1 else (2,) + tuple(shape)) or A.shape[-3:] != tuple(shape):
+        raise ValueError("A and b shapes disagree")
+    B, L, D = shape
+    s0 = _np(s0, np.float64)
+    if s0 is not None and s0.shape != (ns, B, D):
+        raise ValueError("s0 must be [ns][B][D]")
+    s = np.empty(b.shape, np.float64)
+    rc = _load().oracle_scan(ns, B, L, D, _ptr(A), _ptr(b), _ptr(s0), _ptr(s), nthreads or default_threads())
+    if rc:
+        raise ValueError(f"oracle_scan failed ({rc})")
+    return s
 
 
 def flags(max_update, tol=1e-4, early_exit=False):

@@ -457,3 +457,49 @@ int oracle_cell(int cell, int n, const double* s, const double* u, const double*
   }
   return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* O4. The linear recurrence alone (the scan tier). The pages' linear SSM    */
+/* h_l = A_l h_{l-1} + B_l x_l (ParaRNN article, cafecomtech.com, section    */
+/* "O compromisso que SSMs fizeram"), with the input term already formed:    */
+/*   s_l = A_l s_{l-1} + b_l,  l = 0 .. L-1,  s_{-1} = s0 (zero when NULL),  */
+/* per channel (b, d); A_l is a scalar (ns = 1, diagonal cell) or a 2x2      */
+/* block over the channel's two state components (ns = 2), as in section     */
+/* "Engenharia pra escalar". Component-major planes:                          */
+/*   A [ns*ns][B][L][D] (row-major block entries), b and s [ns][B][L][D],      */
+/*   s0 [ns][B][D].                                                           */
+typedef struct {
+  int ns, B, L, D;
+  const double *A, *b, *s0;
+  double* s;
+} scan_ctx;
+
+static void scan_worker(void* vctx, int d_lo, int d_hi) {
+  const scan_ctx* c = (const scan_ctx*)vctx;
+  const size_t plane = (size_t)c->B * c->L * c->D;
+  for (int d = d_lo; d < d_hi; ++d)
+    for (int b = 0; b < c->B; ++b) {
+      double prev[MAXS], next[MAXS];
+      for (int r = 0; r < c->ns; ++r) prev[r] = c->s0 ? c->s0[((size_t)r * c->B + b) * c->D + d] : 0.0;
+      for (int l = 0; l < c->L; ++l) {
+        const size_t at = ((size_t)b * c->L + l) * c->D + d;
+        for (int r = 0; r < c->ns; ++r) {
+          double acc = c->b[(size_t)r * plane + at];
+          for (int q = 0; q < c->ns; ++q) acc += c->A[(size_t)(r * c->ns + q) * plane + at] * prev[q];
+          next[r] = acc;
+        }
+        for (int r = 0; r < c->ns; ++r) {
+          c->s[(size_t)r * plane + at] = next[r];
+          prev[r] = next[r];
+        }
+      }
+    }
+}
+
+int oracle_scan(int ns, int B, int L, int D, const double* A, const double* b, const double* s0, double* s,
+                int nthreads) {
+  if ((ns != 1 && ns != 2) || B <= 0 || L <= 0 || D <= 0 || !A || !b || !s) return -1;
+  scan_ctx c = {ns, B, L, D, A, b, s0, s};
+  parallel_over_d(D, nthreads, scan_worker, &c);
+  return 0;
+}

@@ -35,6 +35,11 @@ MUTANTS = [
      "lam[NS - 1] += (double)c->dh[((size_t)b * L + l) * p->D + d];"),
     ("seq_initial_state_ignored", "for (int k = 0; k < p->NS; ++k) s[k] = p->s0 ?",
      "for (int k = 0; k < p->NS; ++k) s[k] = 0 ?"),
+    ("scan_transposed_block", "acc += c->A[(size_t)(r * c->ns + q) * plane + at] * prev[q];",
+     "acc += c->A[(size_t)(q * c->ns + r) * plane + at] * prev[q];"),
+    ("scan_initial_state_ignored", "prev[r] = c->s0 ? c->s0[((size_t)r * c->B + b) * c->D + d] : 0.0;",
+     "prev[r] = 0.0;"),
+    ("scan_state_not_advanced", "          prev[r] = next[r];\n", "\n"),
 ]
 
 
@@ -57,6 +62,13 @@ def _pins():
              lambda cell=cell: P.test_adjoint_dense_solve_at_newton_iterate(O, cell, 5, 2)),
             (f"dot_{cell}", lambda cell=cell: P.test_adjoint_dot_product_identity(O, cell)),
         ]
+    pins += [
+        ("scan_cumsum", lambda: P.test_scan_unit_coefficient_is_cumulative_sum(O)),
+        ("scan_geometric", lambda: P.test_scan_constant_coefficients_geometric_closed_form(O)),
+        ("scan_rotation", lambda: P.test_scan_block_rotation_closed_form(O)),
+        ("scan_dense_1", lambda: P.test_scan_dense_bidiagonal_solve(O, 1)),
+        ("scan_dense_2", lambda: P.test_scan_dense_bidiagonal_solve(O, 2)),
+    ]
     pins.append(("gru_closed_form", lambda: P.test_gru_linear_cell_closed_form(O)))
     pins.append(("lstm_closed_form", lambda: P.test_lstm_linear_cell_closed_form(O)))
     return pins

@@ -435,3 +435,94 @@ def test_newton_nan_propagates_to_update(oracle_lib):
     out, upd = oracle_lib.newton("gru", u, x.a, K=3)
     assert np.isnan(upd[:, 1]).all() and np.isfinite(upd[:, 0]).all()
     assert np.isnan(out[0, 1, 7:, 2]).all() and np.isfinite(out[0, 0]).all()
+
+
+# ---------------------------------------------------------------------------
+# The linear recurrence alone (O4, the scan tier): s_l = A_l s_{l-1} + b_l.
+
+def test_scan_unit_coefficient_is_cumulative_sum(oracle_lib):
+    """A = 1: s_l = s0 + b_0 + ... + b_l (numpy.cumsum)."""
+    rng = np.random.default_rng(40)
+    B, L, D = 2, 37, 3
+    b = rng.normal(size=(B, L, D))
+    s0 = rng.normal(size=(1, B, D))
+    s = oracle_lib.scan(np.ones((B, L, D)), b, s0)
+    np.testing.assert_allclose(s, s0[0][:, None, :] + np.cumsum(b, axis=1), rtol=0, atol=1e-12)
+
+
+def test_scan_zero_coefficient_returns_inputs(oracle_lib):
+    rng = np.random.default_rng(41)
+    b = rng.normal(size=(2, 9, 4))
+    s = oracle_lib.scan(np.zeros_like(b), b, rng.normal(size=(1, 2, 4)))
+    assert np.array_equal(s, b)
+
+
+def test_scan_constant_coefficients_geometric_closed_form(oracle_lib):
+    """A = alpha, b = beta: s_l = alpha^(l+1) s0 + beta (1 - alpha^(l+1)) / (1 - alpha)."""
+    B, L, D = 1, 50, 3
+    alpha = np.array([0.5, -0.8, 0.97])
+    beta = np.array([1.0, -2.0, 0.25])
+    s0 = np.array([[[0.3, 1.5, -4.0]]])
+    s = oracle_lib.scan(np.broadcast_to(alpha, (B, L, D)), np.broadcast_to(beta, (B, L, D)), s0)
+    p = alpha[None, :] ** (np.arange(1, L + 1)[:, None])  # [L][D]
+    want = p * s0[0, 0] + beta * (1.0 - p) / (1.0 - alpha)
+    np.testing.assert_allclose(s[0], want, rtol=1e-12, atol=1e-12)
+
+
+def test_scan_block_rotation_closed_form(oracle_lib):
+    """A_l = R(theta) (rotation, rows first), b = 0: s_l = R((l+1) theta) s0.
+    A transposed block would rotate the other way."""
+    L, theta = 23, 0.3
+    R = np.array([[np.cos(theta), -np.sin(theta)], [np.sin(theta), np.cos(theta)]])
+    A = np.broadcast_to(R[:, :, None, None, None], (2, 2, 1, L, 1))
+    s = oracle_lib.scan(A, np.zeros((2, 1, L, 1)), np.array([[[1.0]], [[0.0]]]))
+    ang = theta * np.arange(1, L + 1)
+    np.testing.assert_allclose(s[0, 0, :, 0], np.cos(ang), atol=1e-12)
+    np.testing.assert_allclose(s[1, 0, :, 0], np.sin(ang), atol=1e-12)
+
+
+@pytest.mark.parametrize("ns", [1, 2])
+def test_scan_dense_bidiagonal_solve(oracle_lib, ns):
+    """The whole recurrence is one block lower-bidiagonal linear system
+    (I - subdiag(A_1 .. A_{L-1})) s = b + e_0 A_0 s0, solved by numpy.linalg.solve."""
+    rng = np.random.default_rng(42 + ns)
+    L = 7
+    A = rng.uniform(-1.2, 1.2, size=(ns, ns, L))
+    b = rng.normal(size=(ns, L))
+    s0 = rng.normal(size=ns)
+    M = np.eye(L * ns)
+    for l in range(1, L):
+        M[l * ns:(l + 1) * ns, (l - 1) * ns:l * ns] = -A[:, :, l]
+    rhs = b.T.reshape(-1).copy()
+    rhs[:ns] += A[:, :, 0] @ s0
+    want = np.linalg.solve(M, rhs).reshape(L, ns).T  # [ns][L]
+    if ns == 1:
+        s = oracle_lib.scan(A[0, 0][None, :, None], b[0][None, :, None], s0.reshape(1, 1, 1))
+        got = s[:, :, 0]
+    else:
+        s = oracle_lib.scan(A[:, :, None, :, None], b[:, None, :, None], s0.reshape(2, 1, 1))
+        got = s[:, 0, :, 0]
+    np.testing.assert_allclose(got, want, rtol=1e-11, atol=1e-11)
+
+
+def test_scan_block_with_zero_coupling_is_two_diagonal_scans(oracle_lib):
+    rng = np.random.default_rng(44)
+    B, L, D = 2, 15, 3
+    a = rng.uniform(-0.9, 0.9, size=(2, B, L, D))
+    b = rng.normal(size=(2, B, L, D))
+    s0 = rng.normal(size=(2, B, D))
+    A = np.zeros((2, 2, B, L, D))
+    A[0, 0], A[1, 1] = a[0], a[1]
+    s = oracle_lib.scan(A, b, s0)
+    for r in range(2):
+        np.testing.assert_allclose(s[r], oracle_lib.scan(a[r], b[r], s0[r:r + 1]), rtol=0, atol=1e-14)
+
+
+def test_scan_is_linear_in_inputs_and_initial_state(oracle_lib):
+    rng = np.random.default_rng(45)
+    A = rng.uniform(-1, 1, size=(2, 2, 1, 30, 2))
+    b1, b2 = rng.normal(size=(2, 2, 1, 30, 2))
+    s1, s2 = rng.normal(size=(2, 2, 1, 2))
+    lhs = oracle_lib.scan(A, b1 + 2.0 * b2, s1 - s2)
+    rhs = oracle_lib.scan(A, b1, s1) + 2.0 * oracle_lib.scan(A, b2, None) - oracle_lib.scan(A, 0 * b1, s2)
+    np.testing.assert_allclose(lhs, rhs, rtol=1e-12, atol=1e-12)
