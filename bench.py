@@ -79,13 +79,13 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
-def traffic_path(workload: str) -> Path:
-    return ROOT / "profiles" / f"newton_iter_{workload}_traffic.json"
+def traffic_path(workload: str, kernel: str = "newton_iter") -> Path:
+    return ROOT / "profiles" / f"{kernel}_{workload}_traffic.json"
 
 
-def load_traffic(workload: str, digest: str):
+def load_traffic(workload: str, digest: str, kernel: str = "newton_iter"):
     """Counter-measured HBM bytes per launch for the current kernel sources, if profiled."""
-    f = traffic_path(workload)
+    f = traffic_path(workload, kernel)
     if not f.exists():
         return None
     try:
@@ -97,8 +97,9 @@ def load_traffic(workload: str, digest: str):
     return d.get("bytes_per_launch")
 
 
-def traffic_from_counters(workload: str, fetch_csv: str, write_csv: str, iters: int) -> dict:
-    """Per-launch HBM bytes of the Newton-iteration kernel from two rocprofv3
+def traffic_from_counters(workload: str, fetch_csv: str, write_csv: str, iters: int,
+                          kernel: str = "newton_iter") -> dict:
+    """Per-launch HBM bytes of the Newton-iteration (or scan) kernel from two rocprofv3
     --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) of
     `bench.py --copy-calibration`. Each counter is scaled by bytes / counter of
     the 1 GiB device copy in the same run."""
@@ -109,7 +110,7 @@ def traffic_from_counters(workload: str, fetch_csv: str, write_csv: str, iters: 
         rows.sort(key=lambda r: int(r["Dispatch_Id"]))
         copy = [float(r["Counter_Value"]) * 1024 for r in rows
                 if "copyBuffer" in r["Kernel_Name"] and float(r["Counter_Value"]) > 1e5]
-        its = [float(r["Counter_Value"]) * 1024 for r in rows if "newton_iter_kernel" in r["Kernel_Name"]]
+        its = [float(r["Counter_Value"]) * 1024 for r in rows if f"{kernel}_kernel" in r["Kernel_Name"]]
         return copy, its
 
     calib = float(1 << 30)
@@ -185,6 +186,102 @@ def cpu_baseline(w, x, iters, target_s=12.0):
     }
 
 
+# linear scan alone: read NS*NS coefficient planes and NS input planes, write
+# NS state planes, fp32
+def scan_bytes(ns: int) -> int:
+    return 4 * (ns * ns + 2 * ns)
+
+
+def cpu_baseline_scan(w, x, target_s=12.0):
+    """fp64 oracle scan on a sample of batch rows of the same workload (all D)."""
+    from oracle import oracle as O
+
+    nthreads = O.default_threads()
+
+    def run(nb):
+        A = x.A[:nb] if w.ns == 1 else x.A[:, :, :nb]
+        b = x.b[:nb] if w.ns == 1 else x.b[:, :nb]
+        s0 = x.s0[None, :nb] if w.ns == 1 else x.s0[:, :nb]
+        t0 = time.perf_counter()
+        O.scan(A, b, s0, nthreads=nthreads)
+        return time.perf_counter() - t0
+
+    t1 = run(1)
+    nb = int(min(w.B, max(1, target_s / max(t1, 1e-9))))
+    t = run(nb) if nb > 1 else t1
+    elems = nb * w.L * w.D
+    return {"value": elems / t, "unit": "elems/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{nb} of {w.B} batch rows (all D={w.D}, full L={w.L}), fp64 loop; {t:.2f} s"}
+
+
+def bench_scan(w, args):
+    """The linear scan alone (pararnn_scan_diag / pararnn_scan_block2)."""
+    import torch
+    from nonlinear_rnn_solve_newton_amd import binding
+    from nonlinear_rnn_solve_newton_amd.workloads import scan_workload_inputs
+
+    dev = torch.device("cuda:0")
+    x = scan_workload_inputs(w)
+    A, b, s0 = x.A.to(dev), x.b.to(dev), x.s0.to(dev)
+    hip = HipEvents()
+    ev = hip.create(3)
+    first = binding.scan(A, b, s0)
+    ws, out = first["ws"], first["s"]
+    for _ in range(args.warmup):
+        binding.scan(A, b, s0, out=out, ws=ws)
+    torch.cuda.synchronize()
+    scan_ms, clear_ms = [], []
+    for _ in range(args.steps):
+        binding.scan(A, b, s0, out=out, ws=ws, events=ev)
+        clear_ms.append(hip.ms(ev[0], ev[1]))
+        scan_ms.append(hip.ms(ev[1], ev[2]))
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        binding.scan(A, b, s0, out=out, ws=ws)
+    stop.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    mean = lambda v: sum(v) / len(v)  # noqa: E731
+    kms = mean(scan_ms)
+    nbytes = scan_bytes(w.ns) * w.N
+    achieved = nbytes / (kms * 1e-3) / 1e9
+    digest = source_digest()
+    result = {
+        "metric": "scanned state elems/s (B*L*D) of the linear scan s_l = A_l s_{l-1} + b_l",
+        "value": w.N / (ms_step * 1e-3),
+        "unit": "elems/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; A ~ U(-0.95, 0.95) per block row sum, b, s0 ~ N(0,1))",
+        "config": {"workload": w.name, "block": "diag" if w.ns == 1 else "2x2", "B": w.B, "L": w.L, "D": w.D},
+        "roofline": {"bound": "hbm", "kernel": "scan_kernel", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": load_traffic(w.name, digest, "scan"),
+                     "algorithmic_bytes_per_launch": [nbytes], "launch_ms": [kms]},
+        "timing": {"workspace_clear_ms": mean(clear_ms), "scan_ms": kms, "source_digest": digest},
+    }
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = src.numel() * 4
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_scan(w, x)
+    hip.destroy(ev)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,18 +296,23 @@ def main(argv=None):
     ap.add_argument("--stats-summary", metavar="KERNEL_STATS_CSV",
                     help="write profiles/<workload>_kernel_stats.md from a rocprofv3 --stats CSV")
     args = ap.parse_args(argv)
+    sys.path.insert(0, str(ROOT))
+    from nonlinear_rnn_solve_newton_amd.workloads import HEADLINE, SCAN_WORKLOADS, WORKLOADS
+    name = args.workload or HEADLINE
+    if name not in WORKLOADS and name not in SCAN_WORKLOADS:
+        print(json.dumps({"error": f"unknown workload {name}",
+                          "workloads": sorted(WORKLOADS) + sorted(SCAN_WORKLOADS)}))
+        return 2
     if args.stats_summary:
-        sys.path.insert(0, str(ROOT))
-        from nonlinear_rnn_solve_newton_amd.workloads import HEADLINE, WORKLOADS
-        w = WORKLOADS[args.workload or HEADLINE]
-        print(write_stats_summary(w.name, args.stats_summary))
+        print(write_stats_summary(name, args.stats_summary))
         return 0
     if args.traffic_from:
-        sys.path.insert(0, str(ROOT))
-        from nonlinear_rnn_solve_newton_amd.workloads import HEADLINE, WORKLOADS
-        w = WORKLOADS[args.workload or HEADLINE]
-        d = traffic_from_counters(w.name, *args.traffic_from, iters=w.iters)
-        traffic_path(w.name).write_text(json.dumps(d, indent=1) + "\n")
+        if name in SCAN_WORKLOADS:
+            d = traffic_from_counters(name, *args.traffic_from, iters=1, kernel="scan")
+            traffic_path(name, "scan").write_text(json.dumps(d, indent=1) + "\n")
+        else:
+            d = traffic_from_counters(name, *args.traffic_from, iters=WORKLOADS[name].iters)
+            traffic_path(name).write_text(json.dumps(d, indent=1) + "\n")
         print(json.dumps(d))
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -218,13 +320,15 @@ def main(argv=None):
                                    "note, not an implementation", "n_gpus": args.gpus}))
         return 2
 
+    if name in SCAN_WORKLOADS:
+        return bench_scan(SCAN_WORKLOADS[name], args)
+
     import torch
 
-    sys.path.insert(0, str(ROOT))
     from nonlinear_rnn_solve_newton_amd import binding
-    from nonlinear_rnn_solve_newton_amd.workloads import HEADLINE, WORKLOADS, workload_inputs
+    from nonlinear_rnn_solve_newton_amd.workloads import workload_inputs
 
-    w = WORKLOADS[args.workload or HEADLINE]
+    w = WORKLOADS[name]
     K = w.iters
     dev = torch.device("cuda:0")
     x = workload_inputs(w)
@@ -319,8 +423,20 @@ def main(argv=None):
         },
     }
     if w.adjoint:
+        # the same adjoint with the parameter and initial-state gradients
+        # (da, ds0) requested: their partials ride in the reverse scan, plus a
+        # fixed-order reduction launch
+        gfull = binding.adjoint(w.cell, u, a, out["h"], dh, c=out.get("c"), du=gadj["du"],
+                                want_ds0=True, want_da=True)  # a workspace with room for the da partials
+        grad_ms = []
+        for _ in range(args.steps):
+            binding.adjoint(w.cell, u, a, out["h"], dh, c=out.get("c"), ws=gfull["ws"], du=gfull["du"],
+                            want_ds0=True, want_da=True, events=ev_adj)
+            grad_ms.append(hip.ms(ev_adj[1], ev_adj[2]))
+        torch.cuda.synchronize()
         amean = mean(adj_ms)
         result["timing"]["adjoint_ms"] = amean
+        result["timing"]["adjoint_with_da_ds0_ms"] = mean(grad_ms)
         result["adjoint_roofline"] = {
             "bound": "hbm", "kernel": "adjoint_kernel",
             "achieved": adjoint_bytes(w.cell, u_bytes) * N / (amean * 1e-3) / 1e9,

@@ -56,7 +56,12 @@ extern "C" {
 
 typedef enum { PARARNN_F32 = 0, PARARNN_BF16 = 1 } pararnn_dtype;
 typedef enum { PARARNN_GRU = 0, PARARNN_LSTM = 1 } pararnn_cell;
-typedef enum { PARARNN_OP_SOLVE = 0, PARARNN_OP_ADJOINT = 1 } pararnn_op;
+typedef enum {
+  PARARNN_OP_SOLVE = 0,
+  PARARNN_OP_ADJOINT = 1,
+  PARARNN_OP_SCAN_DIAG = 2,   /* pararnn_scan_diag; the cell argument is ignored */
+  PARARNN_OP_SCAN_BLOCK2 = 3  /* pararnn_scan_block2; the cell argument is ignored */
+} pararnn_op;
 
 typedef struct {
   int32_t B, L, D;    /* batch rows, sequence length, channels; all >= 1 */
@@ -110,6 +115,30 @@ int32_t pararnn_adjoint(int32_t cell, const void* u, const float* a, const float
                         const float* h0, const float* c, const float* h, const float* dh,
                         float* du, float* ds0, float* da, void* ws, size_t ws_bytes,
                         const pararnn_opts* o, void* stream);
+
+/* The linear scan alone: the solver step of every Newton iteration, for a
+ * linear SSM the caller has assembled, e.g. from the Jacobians of a cell this
+ * library does not implement (ParaRNN article, cafecomtech.com: section
+ * "O compromisso que SSMs fizeram" for the linear recurrence and its parallel
+ * scan, section "Como usar" for cells supplied by the user). Per channel
+ * (b, d), for l = 0 .. L-1:
+ *   s_l = A_l s_{l-1} + b_l,   s_{-1} = s0 (zero when s0 is NULL).
+ * pararnn_scan_diag: A_l is a scalar (diagonal Jacobian, NS = 1).
+ * pararnn_scan_block2: A_l is a 2x2 block over the channel's two state
+ *   components (NS = 2); s_l[r] = sum_q A_l[r][q] s_{l-1}[q] + b_l[r].
+ * Layouts: component-major fp32 planes of [B][L][D] each (device):
+ *   A  [NS*NS][B][L][D], block entries row-major: A00, A01, A10, A11
+ *   b  [NS][B][L][D],  s (output) [NS][B][L][D],  s0 [NS][B][D] or NULL.
+ * Workspace: pararnn_workspace_bytes(any cell, PARARNN_OP_SCAN_DIAG or
+ * PARARNN_OP_SCAN_BLOCK2, o). opts: B, L, D and events (3 handles: before
+ * the workspace reset, after it, after the scan) are used; the others are
+ * ignored. Non-finite coefficients propagate like any other value. Errors as
+ * for the solves; 16-byte alignment with D divisible by 4 (diag) or 2 (block2)
+ * selects the widest accesses. */
+int32_t pararnn_scan_diag(const float* A, const float* b, const float* s0, float* s, void* ws,
+                          size_t ws_bytes, const pararnn_opts* o, void* stream);
+int32_t pararnn_scan_block2(const float* A, const float* b, const float* s0, float* s, void* ws,
+                            size_t ws_bytes, const pararnn_opts* o, void* stream);
 
 /* Static description of a status code. */
 const char* pararnn_strerror(int32_t status);

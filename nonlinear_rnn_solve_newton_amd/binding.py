@@ -20,7 +20,7 @@ LIB_PATH = PKG / "libpararnn.so"
 HEADER = PKG.parent / "include" / "pararnn.h"
 
 GRU, LSTM = 0, 1
-OP_SOLVE, OP_ADJOINT = 0, 1
+OP_SOLVE, OP_ADJOINT, OP_SCAN_DIAG, OP_SCAN_BLOCK2 = 0, 1, 2, 3
 F32, BF16 = 0, 1
 CELLS = {"gru": GRU, "lstm": LSTM}
 GATES = {"gru": 3, "lstm": 4}
@@ -47,7 +47,7 @@ class Opts(ctypes.Structure):
 def header_functions() -> list[str]:
     """Names of the functions declared in include/pararnn.h."""
     text = HEADER.read_text()
-    return re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?(pararnn_[a-z_]+)\s*\(", text, re.M)
+    return re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?(pararnn_[a-z_0-9]+)\s*\(", text, re.M)
 
 
 _lib = None
@@ -69,6 +69,10 @@ def lib():
         L.pararnn_solve_lstm.restype = I32
         L.pararnn_adjoint.argtypes = [I32, P, P, P, P, P, P, P, P, P, P, P, SZ, OPTP, P]
         L.pararnn_adjoint.restype = I32
+        L.pararnn_scan_diag.argtypes = [P, P, P, P, P, SZ, OPTP, P]
+        L.pararnn_scan_diag.restype = I32
+        L.pararnn_scan_block2.argtypes = [P, P, P, P, P, SZ, OPTP, P]
+        L.pararnn_scan_block2.restype = I32
         L.pararnn_strerror.argtypes = [I32]
         L.pararnn_strerror.restype = ctypes.c_char_p
         _lib = L
@@ -221,3 +225,40 @@ def adjoint(cell: str, u: torch.Tensor, a: torch.Tensor, h: torch.Tensor, dh: to
     del keep
     _check(st, "pararnn_adjoint")
     return dict(du=du, ds0=ds0, da=da, ws=ws)
+
+
+def scan(A: torch.Tensor, b: torch.Tensor, s0: Optional[torch.Tensor] = None, *,
+         out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+         events: Optional[Sequence[int]] = None):
+    """Linear recurrence s_l = A_l s_{l-1} + b_l per channel (pararnn_scan_diag
+    or pararnn_scan_block2, chosen by the shape of A).
+
+    Diagonal: A, b [B][L][D], s0 [B][D]. 2x2 blocks: A [2][2][B][L][D] (block
+    rows first), b [2][B][L][D], s0 [2][B][D]. All fp32 device tensors; s0 may
+    be None (zero). Returns dict(s, ws) with s shaped like b.
+    """
+    _dev(A, "A", torch.float32)
+    if A.dim() == 3:
+        ns, (B, L, D) = 1, A.shape
+    elif A.dim() == 5 and tuple(A.shape[:2]) == (2, 2):
+        ns, (B, L, D) = 2, A.shape[2:]
+    else:
+        raise PararnnError("A must be [B][L][D] or [2][2][B][L][D]")
+    bshape = (B, L, D) if ns == 1 else (2, B, L, D)
+    _dev(b, "b", torch.float32, bshape)
+    _dev(s0, "s0", torch.float32, (B, D) if ns == 1 else (2, B, D))
+    if out is None:
+        out = torch.empty(bshape, dtype=torch.float32, device=A.device)
+    _dev(out, "out", torch.float32, bshape)
+    op = OP_SCAN_DIAG if ns == 1 else OP_SCAN_BLOCK2
+    o, keep = make_opts(B, L, D, 1, 0.0, False, F32, events)
+    need = int(lib().pararnn_workspace_bytes(GRU, op, ctypes.byref(o)))
+    if need == 0:
+        raise PararnnError("invalid sizes")
+    if ws is None:
+        ws = alloc_workspace(need, A.device)
+    fn = lib().pararnn_scan_diag if ns == 1 else lib().pararnn_scan_block2
+    st = fn(_ptr(A), _ptr(b), _ptr(s0), _ptr(out), _ptr(ws), ws.numel(), ctypes.byref(o), _stream(A.device))
+    del keep
+    _check(st, "pararnn_scan_diag" if ns == 1 else "pararnn_scan_block2")
+    return dict(s=out, ws=ws)

@@ -9,6 +9,7 @@
 #include "../../include/pararnn.h"
 #include "adjoint.h"
 #include "newton_iter.h"
+#include "scan.h"
 
 namespace pararnn {
 namespace {
@@ -39,11 +40,41 @@ struct CfgFirst : Cfg<Cell, C, false> {};
 // overhead outweighs the wider loads).
 template <class Cell, bool ADJ> constexpr int max_c() { return Cell::NS == 2 ? 1 : 2; }
 
+// The linear scan alone: NS state components per channel (1: diagonal, 2:
+// 2x2 blocks), C channels per lane. The scan streams 8 (NS = 1) or 24
+// (NS = 2) bytes of coefficients per step and channel and does a few FMAs.
+template <int NS, int C>
+struct ScanCfg;
+template <> struct ScanCfg<1, 4> { static constexpr int T = 8, W = 4, LL = 2, OCC = 3; };
+template <> struct ScanCfg<1, 2> { static constexpr int T = 16, W = 4, LL = 2, OCC = 4; };
+template <> struct ScanCfg<1, 1> { static constexpr int T = 16, W = 4, LL = 1, OCC = 4; };
+template <> struct ScanCfg<2, 2> { static constexpr int T = 8, W = 4, LL = 2, OCC = 2; };
+template <> struct ScanCfg<2, 1> { static constexpr int T = 16, W = 4, LL = 1, OCC = 3; };
+template <int NS> constexpr int scan_max_c() { return NS == 1 ? 4 : 2; }
+
+bool is_scan(int op) { return op == PARARNN_OP_SCAN_DIAG || op == PARARNN_OP_SCAN_BLOCK2; }
+int scan_ns(int op) { return op == PARARNN_OP_SCAN_BLOCK2 ? 2 : 1; }
+
 // workgroup footprint of one configuration: timesteps (one look-back chunk)
 // and channels
 struct Geo {
   int chunk, cw;
 };
+
+template <int NS, int C>
+constexpr Geo scan_geo() {
+  using K = ScanCfg<NS, C>;
+  return Geo{K::T * K::W * K::LL, (64 / K::LL) * C};
+}
+
+template <int NS>
+Geo scan_geo_for_c(int C) {
+  if constexpr (scan_max_c<NS>() >= 4) {
+    if (C == 4) return scan_geo<NS, 4>();
+  }
+  if (C == 2) return scan_geo<NS, 2>();
+  return scan_geo<NS, 1>();
+}
 
 template <class Cell, int C, bool ADJ>
 constexpr Geo geo() {
@@ -63,12 +94,14 @@ Geo geo_for_c(int C) {
 }
 
 Geo geo_for(int cell, int op, int C) {
+  if (is_scan(op)) return scan_ns(op) == 2 ? scan_geo_for_c<2>(C) : scan_geo_for_c<1>(C);
   const bool adj = op == PARARNN_OP_ADJOINT;
   if (cell == PARARNN_LSTM) return adj ? geo_for_c<LstmCell, true>(C) : geo_for_c<LstmCell, false>(C);
   return adj ? geo_for_c<GruCell, true>(C) : geo_for_c<GruCell, false>(C);
 }
 
 int cmax_for(int cell, int op) {
+  if (is_scan(op)) return scan_ns(op) == 2 ? scan_max_c<2>() : scan_max_c<1>();
   const bool adj = op == PARARNN_OP_ADJOINT;
   if (cell == PARARNN_LSTM) return adj ? max_c<LstmCell, true>() : max_c<LstmCell, false>();
   return adj ? max_c<GruCell, true>() : max_c<GruCell, false>();
@@ -87,8 +120,8 @@ int ngates(int cell) { return cell == PARARNN_LSTM ? 4 : 3; }
 
 bool opts_ok(int cell, int op, const pararnn_opts* o) {
   if (!o) return false;
-  if (cell != PARARNN_GRU && cell != PARARNN_LSTM) return false;
-  if (op != PARARNN_OP_SOLVE && op != PARARNN_OP_ADJOINT) return false;
+  if (op != PARARNN_OP_SOLVE && op != PARARNN_OP_ADJOINT && !is_scan(op)) return false;
+  if (!is_scan(op) && cell != PARARNN_GRU && cell != PARARNN_LSTM) return false;  // the scan has no cell
   if (o->B < 1 || o->L < 1 || o->D < 1) return false;
   if (op == PARARNN_OP_SOLVE && (o->max_iters < 1 || o->max_iters > 1000)) return false;
   // element counts must stay addressable with 64-bit offsets and tickets in 32 bits
@@ -106,7 +139,7 @@ bool opts_ok(int cell, int op, const pararnn_opts* o) {
 // (cleared at the start of every call) followed by the ping-pong state buffer.
 Layout layout(int cell, int op, const pararnn_opts* o, bool with_da, Geo g) {
   Layout y;
-  const int NS = nstate(cell), G = ngates(cell);
+  const int NS = is_scan(op) ? scan_ns(op) : nstate(cell), G = ngates(cell);
   const size_t B = o->B, L = o->L, D = o->D;
   const int K = (op == PARARNN_OP_SOLVE) ? o->max_iters : 1;
   y.nchunks = static_cast<int>((L + g.chunk - 1) / g.chunk);
@@ -224,6 +257,56 @@ int launch_adj_any(int dtype, int C, const AdjArgs& a, hipStream_t s) {
   return dtype == PARARNN_BF16 ? launch_adj_c<Cell, bf16>(C, a, s) : launch_adj_c<Cell, float>(C, a, s);
 }
 
+template <int NS, int C>
+int launch_scan(const ScanArgs& a, hipStream_t s) {
+  using K = ScanCfg<NS, C>;
+  const unsigned grid = static_cast<unsigned>(a.B) * a.ntiles_d * static_cast<unsigned>(a.nchunks);
+  const ScanArgs& b = a;
+  hipLaunchKernelGGL((scan_kernel<NS, C, K::T, K::W, K::LL, K::OCC>), dim3(grid), dim3(64 * K::W), 0, s, b);
+  return check_hip(hipGetLastError());
+}
+
+int scan(int ns, const float* A, const float* b, const float* s0, float* s, void* ws, size_t ws_bytes,
+         const pararnn_opts* o, hipStream_t stream) {
+  const int op = ns == 2 ? PARARNN_OP_SCAN_BLOCK2 : PARARNN_OP_SCAN_DIAG;
+  if (!opts_ok(PARARNN_GRU, op, o)) return PARARNN_EINVAL;
+  if (!A || !b || !s || !ws) return PARARNN_EINVAL;
+  const int C = pick_c(cmax_for(PARARNN_GRU, op), o->D, sizeof(float), A, {b, s0, s});
+  if (!C) return PARARNN_EUNSUPPORTED;
+  const Geo g = geo_for(PARARNN_GRU, op, C);
+  // one chunk of a plane is addressed with 32-bit offsets below 2^31
+  if (static_cast<double>(g.chunk) * o->D * 4.0 >= 2147483648.0) return PARARNN_EUNSUPPORTED;
+  const Layout y = layout(PARARNN_GRU, op, o, false, g);
+  if (ws_bytes < y.total) return PARARNN_EWORKSPACE;
+  if (!aligned(ws, kAlign)) return PARARNN_EUNSUPPORTED;
+  char* w = static_cast<char*>(ws);
+
+  int rc = record(o, 0, stream);
+  if (rc) return rc;
+  rc = clear_ws(w, y, nullptr, 0, stream);
+  if (rc) return rc;
+  rc = record(o, 1, stream);
+  if (rc) return rc;
+  ScanArgs sa;
+  memset(&sa, 0, sizeof(sa));
+  sa.A = A;
+  sa.b = b;
+  sa.s0 = s0;
+  sa.s = s;
+  sa.incl = reinterpret_cast<unsigned long long*>(w + y.incl);
+  sa.agg = reinterpret_cast<unsigned long long*>(w + y.agg);
+  sa.ctr = reinterpret_cast<unsigned int*>(w + y.ctr);
+  sa.B = o->B;
+  sa.L = o->L;
+  sa.D = o->D;
+  sa.nchunks = y.nchunks;
+  sa.ntiles_d = y.ntiles_d;
+  if (ns == 2) rc = C == 2 ? launch_scan<2, 2>(sa, stream) : launch_scan<2, 1>(sa, stream);
+  else rc = C == 4 ? launch_scan<1, 4>(sa, stream) : C == 2 ? launch_scan<1, 2>(sa, stream) : launch_scan<1, 1>(sa, stream);
+  if (rc) return rc;
+  return record(o, 2, stream);
+}
+
 int solve(int cell, const void* u, const float* a, const float* c0, const float* h0, float* c, float* h,
           void* ws, size_t ws_bytes, const pararnn_opts* o, int32_t* iters, int32_t* converged,
           float* max_update, hipStream_t stream) {
@@ -313,6 +396,16 @@ extern "C" size_t pararnn_workspace_bytes(int32_t cell, int32_t op, const pararn
     n = t > n ? t : n;
   }
   return n;
+}
+
+extern "C" int32_t pararnn_scan_diag(const float* A, const float* b, const float* s0, float* s, void* ws,
+                                     size_t ws_bytes, const pararnn_opts* o, void* stream) {
+  return scan(1, A, b, s0, s, ws, ws_bytes, o, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int32_t pararnn_scan_block2(const float* A, const float* b, const float* s0, float* s, void* ws,
+                                       size_t ws_bytes, const pararnn_opts* o, void* stream) {
+  return scan(2, A, b, s0, s, ws, ws_bytes, o, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int32_t pararnn_solve_gru(const void* u, const float* a, const float* h0, float* h, void* ws,

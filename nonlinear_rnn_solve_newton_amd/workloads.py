@@ -131,3 +131,59 @@ def gather_channels(x: torch.Tensor, chans: torch.Tensor, D: int) -> torch.Tenso
     d = (chans % D).tolist()
     cols = [x[bi, ..., di] for bi, di in zip(b, d)]  # each [L] or [L][G]
     return torch.stack(cols, dim=-1).unsqueeze(0).contiguous()
+
+
+# ---------------------------------------------------------------------------
+# The linear scan alone. Coefficients drawn so the recurrence stays bounded:
+# A ~ U(-amax, amax) per channel and step (2x2 blocks: each entry
+# U(-amax/2, amax/2), so every row of a block sums to at most amax in
+# magnitude), b ~ N(0, 1), s0 ~ N(0, 1); drawn in that order.
+
+@dataclass(frozen=True)
+class ScanWorkload:
+    name: str
+    ns: int  # 1: diagonal, 2: 2x2 blocks
+    B: int
+    L: int
+    D: int
+    seed: int
+    amax: float = 0.95
+
+    @property
+    def N(self) -> int:
+        return self.B * self.L * self.D
+
+
+SCAN_WORKLOADS = {
+    w.name: w
+    for w in [
+        ScanWorkload("scan_diag_b8_l4096_d1024", 1, 8, 4096, 1024, seed=5),
+        ScanWorkload("scan_block2_b8_l4096_d1024", 2, 8, 4096, 1024, seed=6),
+    ]
+}
+
+
+@dataclass
+class ScanInputs:
+    A: torch.Tensor  # [B][L][D] or [2][2][B][L][D] fp32, CPU
+    b: torch.Tensor  # [B][L][D] or [2][B][L][D] fp32, CPU
+    s0: torch.Tensor  # [B][D] or [2][B][D] fp32, CPU
+
+
+def make_scan_inputs(ns: int, B: int, L: int, D: int, *, seed: int, amax: float = 0.95) -> ScanInputs:
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    if ns == 1:
+        A = amax * (2.0 * torch.rand(B, L, D, generator=g, dtype=torch.float32) - 1.0)
+        b = torch.randn(B, L, D, generator=g, dtype=torch.float32)
+        s0 = torch.randn(B, D, generator=g, dtype=torch.float32)
+    elif ns == 2:
+        A = 0.5 * amax * (2.0 * torch.rand(2, 2, B, L, D, generator=g, dtype=torch.float32) - 1.0)
+        b = torch.randn(2, B, L, D, generator=g, dtype=torch.float32)
+        s0 = torch.randn(2, B, D, generator=g, dtype=torch.float32)
+    else:
+        raise ValueError("ns must be 1 or 2")
+    return ScanInputs(A=A.contiguous(), b=b.contiguous(), s0=s0.contiguous())
+
+
+def scan_workload_inputs(w: ScanWorkload) -> ScanInputs:
+    return make_scan_inputs(w.ns, w.B, w.L, w.D, seed=w.seed, amax=w.amax)

@@ -20,7 +20,7 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = b.header_functions()
     assert set(names) == {"pararnn_workspace_bytes", "pararnn_solve_gru", "pararnn_solve_lstm",
-                          "pararnn_adjoint", "pararnn_strerror"}
+                          "pararnn_adjoint", "pararnn_scan_diag", "pararnn_scan_block2", "pararnn_strerror"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -97,3 +97,33 @@ def test_misaligned_workspace_rejected(lib):
     st = lib.pararnn_solve_gru(ctypes.c_void_p(4096), ctypes.c_void_p(4096), None, ctypes.c_void_p(4096),
                                ctypes.c_void_p(4096 + 16), 1 << 40, ctypes.byref(o), None, None, None, None)
     assert st == -2
+
+
+def test_scan_workspace_bytes(lib):
+    B, L, D = 8, 4096, 1024
+    o, _ = b.make_opts(B, L, D, 0)  # max_iters is not used by the scan
+    diag = lib.pararnn_workspace_bytes(b.GRU, b.OP_SCAN_DIAG, ctypes.byref(o))
+    blk = lib.pararnn_workspace_bytes(b.GRU, b.OP_SCAN_BLOCK2, ctypes.byref(o))
+    assert 0 < diag < blk < 4 * B * L * D  # descriptors only, no state buffer
+    assert lib.pararnn_workspace_bytes(7, b.OP_SCAN_DIAG, ctypes.byref(o)) == diag  # no cell
+    o1, _ = b.make_opts(1, 40, 64, 0)
+    assert lib.pararnn_workspace_bytes(b.GRU, b.OP_SCAN_DIAG, ctypes.byref(o1)) <= 4096  # one chunk
+    o0, _ = b.make_opts(B, 0, D, 0)
+    assert lib.pararnn_workspace_bytes(b.GRU, b.OP_SCAN_DIAG, ctypes.byref(o0)) == 0
+
+
+@pytest.mark.parametrize("fn", ["pararnn_scan_diag", "pararnn_scan_block2"])
+def test_scan_invalid_arguments_rejected_before_launch(lib, fn):
+    f = getattr(lib, fn)
+    P = lambda v: ctypes.c_void_p(v * 4096) if v else None  # noqa: E731  (never dereferenced)
+
+    def st(A=1, bb=1, s=1, ws=2, ws_bytes=1 << 40, B=2, L=8, D=4, ws_off=0):
+        o, _ = b.make_opts(B, L, D, 0)
+        wsp = ctypes.c_void_p(ws * 4096 + ws_off) if ws else None
+        return f(P(A), P(bb), None, P(s), wsp, ws_bytes, ctypes.byref(o), None)
+
+    assert st(A=0) == -1 and st(bb=0) == -1 and st(s=0) == -1 and st(ws=0) == -1
+    assert st(B=0) == -1 and st(L=-1) == -1 and st(D=0) == -1
+    assert st(ws_bytes=0) == -3
+    assert st(ws_off=16) == -2
+    assert f(P(1), P(1), None, P(1), P(2), 1 << 40, None, None) == -1

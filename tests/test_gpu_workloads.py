@@ -81,3 +81,22 @@ def test_workload_parity(name):
         du_got = g["du"][bidx, :, :, didx].permute(1, 2, 0).cpu().double().numpy()[None]
         gerr = assert_close(du_got, du_want, 1e-4, f"{name} sampled du")
         say(f"workload {name}: sampled du max err {gerr:.2e}")
+
+        # da and ds0 at full size: da[:, d] sums over every row b and step l,
+        # so the oracle solves all B rows of a few sampled channels d
+        say(f"workload {name}: adjoint with da and ds0")
+        g2 = binding.adjoint(w.cell, u, a, r["h"], dh, c=r.get("c"), want_ds0=True, want_da=True)
+        torch.cuda.synchronize()
+        dsel = sorted(np.random.default_rng(11).choice(w.D, 4, replace=False).tolist())
+        chans2 = torch.tensor([b * w.D + d for d in dsel for b in range(w.B)])
+        us2 = gather_channels(x.u, chans2, w.D)
+        as2 = x.a[:, chans2 % w.D].contiguous()
+        want2, _ = O.newton(w.cell, us2, as2, K=w.iters)
+        _, ds0_want, da_cols = O.adjoint(w.cell, us2, as2, want2, gather_channels(x.dh, chans2, w.D))
+        da_want = da_cols.reshape(da_cols.shape[0], len(dsel), w.B).sum(axis=2)  # [G][n_d]
+        da_got = g2["da"][:, dsel].cpu().double().numpy()
+        scale = max(1.0, float(np.abs(da_want).max()))
+        assert_close(da_got, da_want, 1e-4 * scale, f"{name} da at sampled channels")
+        ds0_got = g2["ds0"][:, :, dsel].permute(0, 2, 1).reshape(ds0_want.shape[0], 1, -1).cpu().double().numpy()
+        assert_close(ds0_got, ds0_want, 1e-4, f"{name} ds0 at sampled channels")
+        assert torch.equal(g2["du"], g["du"])  # requesting da and ds0 leaves du unchanged
