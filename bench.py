@@ -282,6 +282,43 @@ def bench_scan(w, args):
     return 0
 
 
+def bench_generic(w, args):
+    """The workload's cell written as a user cell in torch, solved by the
+    generic tier; reported next to the fused kernels, not instead of them."""
+    import torch
+    from nonlinear_rnn_solve_newton_amd import generic
+    from nonlinear_rnn_solve_newton_amd.workloads import workload_inputs
+
+    dev = torch.device("cuda:0")
+    x = workload_inputs(w)
+    u, a = x.u.to(dev), x.a.to(dev)
+    if w.cell == "gru":
+        run = lambda: generic.newton_solve(lambda h, uu: generic.gru_step(h, uu, a), u,  # noqa: E731
+                                           B=w.B, L=w.L, D=w.D, iters=w.iters)
+    else:
+        run = lambda: generic.newton_solve(lambda s, uu: generic.lstm_step(s, uu, a), u,  # noqa: E731
+                                           B=w.B, L=w.L, D=w.D, iters=w.iters, block=2)
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        run()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    print(json.dumps({
+        "metric": "solved state elems/s (B*L*D) per 3-Newton solve, generic-cell tier",
+        "value": w.N / (ms * 1e-3), "unit": "elems/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic (same inputs as the fused workload)",
+        "config": {"workload": w.name, "tier": "generic: torch cell, torch.func.jvp Jacobian, "
+                   "pararnn_scan_diag / pararnn_scan_block2 per iteration"},
+    }), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -289,6 +326,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--generic", action="store_true",
+                    help="run the workload's cell through the generic-cell tier (torch cell + forward-mode "
+                         "AD Jacobian + the library's scan) instead of the fused kernels")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration for profiling)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -322,6 +362,8 @@ def main(argv=None):
 
     if name in SCAN_WORKLOADS:
         return bench_scan(SCAN_WORKLOADS[name], args)
+    if args.generic:
+        return bench_generic(WORKLOADS[name], args)
 
     import torch
 

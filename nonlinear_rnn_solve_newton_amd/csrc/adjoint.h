@@ -345,16 +345,36 @@ __global__ void __launch_bounds__(64 * W, OCC) adjoint_kernel(const AdjArgs p) {
   }
 }
 
-// da[g][d] = sum over chunks and rows of the partials, in a fixed order.
-__global__ void __launch_bounds__(256) da_reduce_kernel(const float* part, float* da, int nchunks,
-                                                        int B, int G, int D) {
-  const long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= static_cast<long long>(G) * D) return;
-  const int g = static_cast<int>(i / D), d = static_cast<int>(i - static_cast<long long>(g) * D);
+// da[g][d] = sum of the per-workgroup partials over all chunks and batch rows,
+// in a fixed order: the partials form rows of G*D columns; row group q of a
+// column adds rows q, q + RG, q + 2 RG, ... in turn (eight loads in flight),
+// then the RG group sums of the column are added in order of q.
+constexpr int kDaCols = 64, kDaGroups = 16;
+__global__ void __launch_bounds__(kDaCols * kDaGroups) da_reduce_kernel(const float* part, float* da, int rows,
+                                                                        long long GD) {
+  __shared__ float s_sum[kDaGroups][kDaCols];
+  const int j = threadIdx.x % kDaCols, q = threadIdx.x / kDaCols;
+  const long long col = static_cast<long long>(blockIdx.x) * kDaCols + j;
   float acc = 0.0f;
-  for (int k = 0; k < nchunks; ++k)
-    for (int b = 0; b < B; ++b) acc += part[((static_cast<long long>(k) * B + b) * G + g) * D + d];
-  da[i] = acc;
+  if (col < GD) {
+    constexpr int U = 8;
+    int r = q;
+    for (; r + (U - 1) * kDaGroups < rows; r += U * kDaGroups) {
+      float v[U];
+#pragma unroll
+      for (int i = 0; i < U; ++i) v[i] = part[static_cast<long long>(r + i * kDaGroups) * GD + col];
+#pragma unroll
+      for (int i = 0; i < U; ++i) acc += v[i];
+    }
+    for (; r < rows; r += kDaGroups) acc += part[static_cast<long long>(r) * GD + col];
+  }
+  s_sum[q][j] = acc;
+  __syncthreads();
+  if (q == 0 && col < GD) {
+    float t = 0.0f;
+    for (int k = 0; k < kDaGroups; ++k) t += s_sum[k][j];
+    da[col] = t;
+  }
 }
 
 }  // namespace pararnn

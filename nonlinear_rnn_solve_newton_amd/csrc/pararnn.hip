@@ -477,8 +477,9 @@ extern "C" int32_t pararnn_adjoint(int32_t cell, const void* u, const float* a, 
   if (da) {
     const int G = ngates(cell);
     const long long n = static_cast<long long>(G) * o->D;
-    hipLaunchKernelGGL(da_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream,
-                       reinterpret_cast<const float*>(w + y.dapart), da, y.nchunks, o->B, G, o->D);
+    hipLaunchKernelGGL(da_reduce_kernel, dim3(static_cast<unsigned>((n + kDaCols - 1) / kDaCols)),
+                       dim3(kDaCols * kDaGroups), 0, stream, reinterpret_cast<const float*>(w + y.dapart), da,
+                       y.nchunks * o->B, n);
     rc = check_hip(hipGetLastError());
     if (rc) return rc;
   }
