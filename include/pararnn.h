@@ -55,6 +55,17 @@ extern "C" {
 #define PARARNN_EHIP (-4)         /* a HIP launch or runtime call failed */
 
 typedef enum { PARARNN_F32 = 0, PARARNN_BF16 = 1 } pararnn_dtype;
+
+/* How a solve is laid out in launches (opts.schedule). */
+typedef enum {
+  PARARNN_SCHEDULE_AUTO = 0,          /* FUSED, or PER_ITERATION when early_exit is set */
+  PARARNN_SCHEDULE_FUSED = 1,         /* all K iterations in one launch; the iterate stays on
+                                         chip between iterations and only iterate K is written
+                                         (ParaRNN article, cafecomtech.com, section "Engenharia
+                                         pra escalar": Newton, assembly and reduction fused);
+                                         not combinable with early_exit */
+  PARARNN_SCHEDULE_PER_ITERATION = 2  /* one fused launch per iteration, iterates through HBM */
+} pararnn_schedule;
 typedef enum { PARARNN_GRU = 0, PARARNN_LSTM = 1 } pararnn_cell;
 typedef enum {
   PARARNN_OP_SOLVE = 0,
@@ -72,8 +83,10 @@ typedef struct {
   int32_t u_dtype;    /* pararnn_dtype of u */
   void* const* events; /* optional: K + 2 hipEvent_t handles recorded on `stream`
                           before the workspace reset, after it, and after each
-                          iteration (solve) / the adjoint launch (adjoint: 3 events);
-                          NULL = none */
+                          iteration (solve; with the fused schedule all K after
+                          its one launch) / the adjoint launch (adjoint: 3
+                          events); NULL = none */
+  int32_t schedule;    /* pararnn_schedule of a solve; ignored by the other calls */
 } pararnn_opts;
 
 /* Bytes of workspace a call with these options needs (depends on the cell,

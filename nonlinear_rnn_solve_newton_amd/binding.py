@@ -41,7 +41,11 @@ class Opts(ctypes.Structure):
         ("early_exit", ctypes.c_int32),
         ("u_dtype", ctypes.c_int32),
         ("events", ctypes.c_void_p),
+        ("schedule", ctypes.c_int32),
     ]
+
+
+SCHEDULES = {"auto": 0, "fused": 1, "per_iteration": 2}
 
 
 def header_functions() -> list[str]:
@@ -114,8 +118,8 @@ def _u_dtype(u: torch.Tensor) -> int:
     raise PararnnError(f"u must be float32 or bfloat16, got {u.dtype}")
 
 
-def make_opts(B, L, D, iters=3, tol=1e-4, early_exit=False, u_dtype=BF16, events=None):
-    o = Opts(B, L, D, iters, tol, int(bool(early_exit)), u_dtype, None)
+def make_opts(B, L, D, iters=3, tol=1e-4, early_exit=False, u_dtype=BF16, events=None, schedule="auto"):
+    o = Opts(B, L, D, iters, tol, int(bool(early_exit)), u_dtype, None, SCHEDULES[schedule])
     keep = None
     if events is not None:
         keep = (ctypes.c_void_p * len(events))(*events)
@@ -140,7 +144,7 @@ def _stream(device):
 
 def solve(cell: str, u: torch.Tensor, a: torch.Tensor, *, h0=None, c0=None, iters: int = 3,
           tol: float = 1e-4, early_exit: bool = False, ws: Optional[torch.Tensor] = None,
-          out=None, events: Optional[Sequence[int]] = None):
+          out=None, events: Optional[Sequence[int]] = None, schedule: str = "auto"):
     """Newton solve; returns dict(h, c (LSTM), iters, converged, max_update) on u's device."""
     G, NS = GATES[cell], NSTATE[cell]
     _dev(u, "u")
@@ -161,7 +165,7 @@ def solve(cell: str, u: torch.Tensor, a: torch.Tensor, *, h0=None, c0=None, iter
     it = torch.empty(1, dtype=torch.int32, device=dev)
     conv = torch.empty(B, dtype=torch.int32, device=dev)
     mu = torch.empty(iters, B, dtype=torch.float32, device=dev)
-    o, keep = make_opts(B, L, D, iters, tol, early_exit, udt, events)
+    o, keep = make_opts(B, L, D, iters, tol, early_exit, udt, events, schedule)
     need = int(lib().pararnn_workspace_bytes(CELLS[cell], OP_SOLVE, ctypes.byref(o)))
     if need == 0:
         raise PararnnError("invalid sizes or iteration count")

@@ -1,0 +1,305 @@
+// newton_fused.h -- all K Newton iterations of the ParaRNN solve in one launch
+// (the fully fused form: Newton, Jacobian assembly and the parallel reduction
+// in one kernel, ParaRNN article, cafecomtech.com, section "Engenharia pra
+// escalar").
+//
+// Each workgroup owns one (chunk, channel tile) for the whole solve and keeps
+// its iterate in registers from iteration to iteration; the intermediate
+// iterates never reach HBM, and only the K-th is stored. Iteration k is the
+// update form of the one-launch kernel (newton_iter.h): d_l = J_l d_{l-1} + r_l
+// with r_l = f(S^(k-1)_{l-1}, u_l) - S^(k-1)_l. What crosses lane, wave and
+// workgroup boundaries between iterations is the iterate at the row before a
+// lane's first step:
+//   - inside a workgroup, the previous lane group's last state, through LDS;
+//   - at the chunk boundary, S^(k)_{c CL - 1}, which the workgroup builds from
+//     its own carry-ins: the carry entering the chunk in iteration k is
+//     exactly d^(k) at that row, so S^(k) = S^(k-1) + carry_k there (S^(0) = 0;
+//     the first chunk sees the fixed initial state).
+// Every iteration has its own descriptor slots, so a predecessor that runs
+// ahead never overwrites what a later chunk still has to read; workgroups
+// take tickets in chunk-major order and only ever wait for earlier tickets,
+// so no residency of the whole grid is needed.
+//
+// UKEEP: keep the gate inputs in registers for all iterations (one HBM read
+// per solve) or stream them again in every iteration (fewer registers).
+#pragma once
+
+#include "newton_iter.h"
+
+namespace pararnn {
+
+struct FusedArgs {
+  const void* u;             // [B][L][G][D] fp32 or bf16
+  const float* a;            // [G][D]
+  const float* s0[2];        // initial state per component [B][D]; nullptr = 0
+  float* sout[2];            // iterate K per component [B][L][D]
+  unsigned long long* incl;  // [K][nchunks][NS][slots]
+  unsigned long long* agg;   // [K][nchunks][NS*NS+NS][slots]
+  unsigned int* ctr;         // [0] ticket
+  unsigned int* pmax;        // [K][B][nchunks][ntiles_d] per-workgroup max |update| bits
+  int B, L, D, K, nchunks, ntiles_d;
+};
+
+template <class Cell, class UT, int C, int T, int W, int LL, int OCC, bool UKEEP>
+__global__ void __launch_bounds__(64 * W, OCC) newton_fused_kernel(const FusedArgs p) {
+  constexpr int NS = Cell::NS, G = Cell::G;
+  constexpr int LD = 64 / LL, CW = LD * C, CL = W * LL * T, NA = NS * NS + NS, NSEG = W * LL;
+
+  __shared__ float s_agg[W][NA][CW];
+  __shared__ float s_carry[NS][CW];
+  __shared__ float s_last[NSEG][NS][CW];
+  __shared__ unsigned int s_ticket;
+  __shared__ uint32_t s_wmax[W];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int ld = lane % LD, ll = lane / LD;
+  const int q = wave * LL + ll;  // lane group in scan order
+  if (tid == 0) s_ticket = atomicAdd(p.ctr, 1u);
+  __syncthreads();
+  const unsigned int ticket = s_ticket;
+  const unsigned int ntiles = static_cast<unsigned int>(p.B) * p.ntiles_d;
+  const int chunk = static_cast<int>(ticket / ntiles);
+  const int tile = static_cast<int>(ticket - static_cast<unsigned int>(chunk) * ntiles);
+  const int b = tile / p.ntiles_d;
+  const int dt0 = (tile - b * p.ntiles_d) * CW;
+  const int d0 = dt0 + ld * C;
+  const bool dv = d0 < p.D;
+  const int lt0 = q * T;
+  const int l0 = chunk * CL + lt0;
+  const long long BD = static_cast<long long>(p.B) * p.ntiles_d * CW;
+  const long long chan = static_cast<long long>(tile) * CW + ld;
+  const long long inc_k = static_cast<long long>(p.nchunks) * NS * BD;  // words per iteration
+  const long long agg_k = static_cast<long long>(p.nchunks) * NA * BD;
+  const long long wrow = static_cast<long long>(b) * p.L + static_cast<long long>(chunk) * CL;
+  const uint32_t ustep = static_cast<uint32_t>(G * p.D * sizeof(UT));
+  const uint32_t gstep = static_cast<uint32_t>(p.D * sizeof(UT));
+  const uint32_t sstep = static_cast<uint32_t>(p.D * sizeof(float));
+  const uint32_t rows = static_cast<uint32_t>(min(p.L - chunk * CL, CL));
+  constexpr uint32_t kOOB = 0x80000000u;  // extents stay below 2^31 bytes
+  const uint32_t vu0 = dv ? static_cast<uint32_t>(lt0) * ustep + static_cast<uint32_t>(d0 * sizeof(UT)) : kOOB;
+  const uint32_t vs0 = dv ? static_cast<uint32_t>(lt0) * sstep + static_cast<uint32_t>(d0 * sizeof(float)) : kOOB;
+  const __amdgpu_buffer_rsrc_t ru =
+      make_rsrc(reinterpret_cast<const char*>(p.u) + wrow * G * p.D * static_cast<long long>(sizeof(UT)), rows * ustep);
+  __amdgpu_buffer_rsrc_t rout[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) rout[s] = make_rsrc(p.sout[s] + wrow * p.D, rows * sstep);
+  const int dc = dv ? d0 : p.D - C;  // channel group for the per-channel loads
+
+  auto tile_body = [&](auto full_tag) {
+  constexpr bool FULL = decltype(full_tag)::value;
+  float av[G][C];
+#pragma unroll
+  for (int g = 0; g < G; ++g) ld_f32<C>(p.a + static_cast<long long>(g) * p.D + dc, av[g]);
+  URaw<UT, C> uu[UKEEP ? T : 1][G];
+  if constexpr (UKEEP) {
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int g = 0; g < G; ++g) uu[t][g].load(ru, vu0 + t * ustep, static_cast<uint32_t>(g) * gstep);
+  }
+  // iterate k-1 at the lane's steps (S^(0) = 0) and at the chunk boundary
+  float so[T][NS][C];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int c = 0; c < C; ++c) so[t][s][c] = 0.0f;
+  float sb[NS][C];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) sb[s][c] = 0.0f;
+    if (chunk == 0 && p.s0[s]) ld_f32<C>(p.s0[s] + static_cast<long long>(b) * p.D + dc, sb[s]);
+  }
+
+  // one Newton iteration; ZERO: the first, evaluated at the zero iterate
+  // (reduced cell form from a lane's third step on, as in newton_iter.h)
+  auto iterate = [&](int k, auto zero_tag) {
+    constexpr bool ZERO = decltype(zero_tag)::value;
+    const uint32_t tag = static_cast<uint32_t>(k);
+    float sp[NS][C];  // iterate k-1 at the row before the lane's first step
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int c = 0; c < C; ++c) sp[s][c] = (q == 0) ? sb[s][c] : (ZERO ? 0.0f : s_last[q - 1][s][ld * C + c]);
+    float Jt[T][NS][NS][C], rt[T][NS][C];
+    Aff<NS, C> acc;
+    acc.set_identity();
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      URaw<UT, C> ut[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        if constexpr (UKEEP) ut[g] = uu[t][g];
+        else ut[g].load(ru, vu0 + t * ustep, static_cast<uint32_t>(g) * gstep);
+      }
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        float ac[G], uc[G], pc[NS], f[NS], J[NS][NS];
+#pragma unroll
+        for (int g = 0; g < G; ++g) { ac[g] = av[g][c]; uc[g] = ut[g].get(c); }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) pc[s] = (t == 0) ? sp[s][c] : so[t - 1][s][c];
+        if (ZERO && t > 1) Cell::step_zero(ac, uc, f, J);
+        else Cell::step(ac, uc, pc, f, J);
+#pragma unroll
+        for (int r = 0; r < NS; ++r) {
+#pragma unroll
+          for (int s = 0; s < NS; ++s) Jt[t][r][s][c] = J[r][s];
+          rt[t][r][c] = ZERO ? f[r] : f[r] - so[t][r][c];
+        }
+      }
+      acc.pre(Jt[t], rt[t]);
+    }
+
+    Aff<NS, C> excl;
+    excl.set_identity();
+    if constexpr (LL > 1) {
+#pragma unroll
+      for (int off = 1; off < LL; off *= 2) {
+        const Aff<NS, C> prev = acc.shfl_up(off * LD);
+        if (ll >= off) acc.after(prev);
+      }
+      const Aff<NS, C> prev = acc.shfl_up(LD);
+      if (ll > 0) excl = prev;
+    }
+    if (ll == LL - 1) {
+#pragma unroll
+      for (int r = 0; r < NS; ++r)
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+#pragma unroll
+          for (int s = 0; s < NS; ++s) s_agg[wave][r * NS + s][ld * C + c] = acc.A[r][s][c];
+          s_agg[wave][NS * NS + r][ld * C + c] = acc.b[r][c];
+        }
+    }
+    __syncthreads();
+
+    if (wave == 0 && ll == 0) {
+      float carry[NS][C];
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int c = 0; c < C; ++c) carry[s][c] = 0.0f;
+      if (dv && p.nchunks > 1) {
+        Aff<NS, C> tot;
+        tot.set_identity();
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+          Aff<NS, C> e;
+#pragma unroll
+          for (int r = 0; r < NS; ++r)
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+#pragma unroll
+              for (int s = 0; s < NS; ++s) e.A[r][s][c] = s_agg[w][r * NS + s][ld * C + c];
+              e.b[r][c] = s_agg[w][NS * NS + r][ld * C + c];
+            }
+          e.after(tot);
+          tot = e;
+        }
+        unsigned long long* incl = p.incl + (k - 1) * inc_k;
+        unsigned long long* agg = p.agg + (k - 1) * agg_k;
+        if (chunk > 0) {
+          if (chunk < p.nchunks - 1) publish_agg<NS, C>(agg, BD, chan, LD, chunk, tag, tot);
+          lookback<NS, C>(incl, agg, BD, chan, LD, chunk, -1, p.nchunks, tag, carry);
+        }
+        if (chunk < p.nchunks - 1) {
+          float x[NS][C];
+#pragma unroll
+          for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int c = 0; c < C; ++c) x[s][c] = carry[s][c];
+          tot.apply(x);
+          publish_incl<NS, C>(incl, BD, chan, LD, chunk, tag, x);
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int c = 0; c < C; ++c) s_carry[s][ld * C + c] = carry[s][c];
+    }
+    __syncthreads();
+
+    float x[NS][C];
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int c = 0; c < C; ++c) x[s][c] = s_carry[s][ld * C + c];
+    // the chunk boundary moves by the carry entering the chunk
+    if (q == 0) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int c = 0; c < C; ++c) sb[s][c] += x[s][c];
+    }
+    for (int w = 0; w < wave; ++w) {
+      Aff<NS, C> e;
+#pragma unroll
+      for (int r = 0; r < NS; ++r)
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+#pragma unroll
+          for (int s = 0; s < NS; ++s) e.A[r][s][c] = s_agg[w][r * NS + s][ld * C + c];
+          e.b[r][c] = s_agg[w][NS * NS + r][ld * C + c];
+        }
+      e.apply(x);
+    }
+    if constexpr (LL > 1) excl.apply(x);
+
+    float mx = 0.0f;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      float y[NS][C];
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int r = 0; r < NS; ++r) {
+          float a2 = rt[t][r][c];
+#pragma unroll
+          for (int s = 0; s < NS; ++s) a2 = fmaf(Jt[t][r][s][c], x[s][c], a2);
+          y[r][c] = a2;
+        }
+      const bool valid = FULL || (dv && l0 + t < p.L);
+#pragma unroll
+      for (int r = 0; r < NS; ++r)
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+          x[r][c] = y[r][c];
+          so[t][r][c] = ZERO ? y[r][c] : so[t][r][c] + y[r][c];
+          if (valid) mx = __builtin_elementwise_maximum(mx, fabsf(y[r][c]));
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int c = 0; c < C; ++c) s_last[q][s][ld * C + c] = so[T - 1][s][c];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, off, 64));
+    if (lane == 0) s_wmax[wave] = __float_as_uint(mx);
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t m = s_wmax[0];
+#pragma unroll
+      for (int w = 1; w < W; ++w) m = max(m, s_wmax[w]);
+      p.pmax[((static_cast<long long>(k - 1) * p.B + b) * p.nchunks + chunk) * p.ntiles_d + dt0 / CW] = m;
+    }
+  };
+
+  iterate(1, std::true_type{});
+  for (int k = 2; k <= p.K; ++k) iterate(k, std::false_type{});
+
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int s = 0; s < NS; ++s) buf_st_f32<C>(rout[s], vs0 + t * sstep, 0u, so[t][s]);  // dropped past L or D
+  };
+
+  const bool full = (chunk + 1) * CL <= p.L && dt0 + CW <= p.D;
+  if (full) tile_body(std::true_type{});
+  else tile_body(std::false_type{});
+}
+
+}  // namespace pararnn

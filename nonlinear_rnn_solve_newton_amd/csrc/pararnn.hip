@@ -8,6 +8,7 @@
 
 #include "../../include/pararnn.h"
 #include "adjoint.h"
+#include "newton_fused.h"
 #include "newton_iter.h"
 #include "scan.h"
 
@@ -28,6 +29,14 @@ template <> struct Cfg<LstmCell, 1, false> { static constexpr int T = 24, W = 4,
 template <> struct Cfg<GruCell, 2, true> { static constexpr int T = 8, W = 4, LL = 2, OCC = 3; };
 template <> struct Cfg<GruCell, 1, true> { static constexpr int T = 8, W = 8, LL = 2, OCC = 2; };
 template <> struct Cfg<LstmCell, 1, true> { static constexpr int T = 16, W = 4, LL = 1, OCC = 2; };
+// All K iterations in one launch (newton_fused.h): the iterate stays in
+// registers between iterations; UKEEP also keeps the gate inputs there.
+template <class Cell, int C>
+struct FusedCfg;
+template <> struct FusedCfg<GruCell, 2> { static constexpr int T = 12, W = 4, LL = 2, OCC = 2; static constexpr bool UKEEP = true; };
+template <> struct FusedCfg<GruCell, 1> { static constexpr int T = 16, W = 4, LL = 1, OCC = 2; static constexpr bool UKEEP = true; };
+template <> struct FusedCfg<LstmCell, 1> { static constexpr int T = 10, W = 4, LL = 1, OCC = 2; static constexpr bool UKEEP = true; };
+
 // Iteration 1 (no state input, lighter cell form): same chunk length and
 // channel tile, its own split into waves and steps.
 template <class Cell, int C>
@@ -45,10 +54,10 @@ template <class Cell, bool ADJ> constexpr int max_c() { return Cell::NS == 2 ? 1
 // (NS = 2) bytes of coefficients per step and channel and does a few FMAs.
 template <int NS, int C>
 struct ScanCfg;
-template <> struct ScanCfg<1, 4> { static constexpr int T = 8, W = 4, LL = 2, OCC = 3; };
+template <> struct ScanCfg<1, 4> { static constexpr int T = 16, W = 8, LL = 1, OCC = 2; };
 template <> struct ScanCfg<1, 2> { static constexpr int T = 16, W = 4, LL = 2, OCC = 4; };
 template <> struct ScanCfg<1, 1> { static constexpr int T = 16, W = 4, LL = 1, OCC = 4; };
-template <> struct ScanCfg<2, 2> { static constexpr int T = 8, W = 4, LL = 2, OCC = 2; };
+template <> struct ScanCfg<2, 2> { static constexpr int T = 8, W = 8, LL = 1, OCC = 2; };
 template <> struct ScanCfg<2, 1> { static constexpr int T = 16, W = 4, LL = 1, OCC = 3; };
 template <int NS> constexpr int scan_max_c() { return NS == 1 ? 4 : 2; }
 
@@ -93,6 +102,24 @@ Geo geo_for_c(int C) {
   return geo<Cell, 1, ADJ>();
 }
 
+template <class Cell, int C>
+constexpr Geo fused_geo() {
+  using K = FusedCfg<Cell, C>;
+  return Geo{K::T * K::W * K::LL, (64 / K::LL) * C};
+}
+
+template <class Cell>
+Geo fused_geo_for_c(int C) {
+  if constexpr (max_c<Cell, false>() >= 2) {
+    if (C == 2) return fused_geo<Cell, 2>();
+  }
+  return fused_geo<Cell, 1>();
+}
+
+Geo fused_geo_for(int cell, int C) {
+  return cell == PARARNN_LSTM ? fused_geo_for_c<LstmCell>(C) : fused_geo_for_c<GruCell>(C);
+}
+
 Geo geo_for(int cell, int op, int C) {
   if (is_scan(op)) return scan_ns(op) == 2 ? scan_geo_for_c<2>(C) : scan_geo_for_c<1>(C);
   const bool adj = op == PARARNN_OP_ADJOINT;
@@ -124,6 +151,10 @@ bool opts_ok(int cell, int op, const pararnn_opts* o) {
   if (!is_scan(op) && cell != PARARNN_GRU && cell != PARARNN_LSTM) return false;  // the scan has no cell
   if (o->B < 1 || o->L < 1 || o->D < 1) return false;
   if (op == PARARNN_OP_SOLVE && (o->max_iters < 1 || o->max_iters > 1000)) return false;
+  if (op == PARARNN_OP_SOLVE &&
+      (o->schedule < PARARNN_SCHEDULE_AUTO || o->schedule > PARARNN_SCHEDULE_PER_ITERATION ||
+       (o->schedule == PARARNN_SCHEDULE_FUSED && o->early_exit)))
+    return false;
   // element counts must stay addressable with 64-bit offsets and tickets in 32 bits
   const double n = static_cast<double>(o->B) * o->L * o->D * 4;
   if (n > 9.0e18) return false;
@@ -137,7 +168,9 @@ bool opts_ok(int cell, int op, const pararnn_opts* o) {
 
 // Workspace: [counters | row maxima | incl descriptors | agg descriptors | da partials]
 // (cleared at the start of every call) followed by the ping-pong state buffer.
-Layout layout(int cell, int op, const pararnn_opts* o, bool with_da, Geo g) {
+// fused: the one-launch schedule of the solve (descriptor slots for every
+// iteration, no state buffer)
+Layout layout(int cell, int op, const pararnn_opts* o, bool with_da, Geo g, bool fused = false) {
   Layout y;
   const int NS = is_scan(op) ? scan_ns(op) : nstate(cell), G = ngates(cell);
   const size_t B = o->B, L = o->L, D = o->D;
@@ -154,14 +187,15 @@ Layout layout(int cell, int op, const pararnn_opts* o, bool with_da, Geo g) {
   if (op == PARARNN_OP_SOLVE) off = round_up(off + sizeof(uint32_t) * static_cast<size_t>(K) * nwg);
   y.incl = off;
   const size_t slots = B * static_cast<size_t>(y.ntiles_d) * g.cw;  // descriptor slots per component
-  if (y.nchunks > 1) off = round_up(off + sizeof(uint64_t) * y.nchunks * NS * slots);
+  const size_t nk = fused ? static_cast<size_t>(K) : 1;  // descriptor sets
+  if (y.nchunks > 1) off = round_up(off + sizeof(uint64_t) * nk * y.nchunks * NS * slots);
   y.agg = off;
-  if (y.nchunks > 1) off = round_up(off + sizeof(uint64_t) * y.nchunks * (NS * NS + NS) * slots);
+  if (y.nchunks > 1) off = round_up(off + sizeof(uint64_t) * nk * y.nchunks * (NS * NS + NS) * slots);
   y.zero_end = off;
   y.dapart = off;
   if (op == PARARNN_OP_ADJOINT && with_da) off = round_up(off + sizeof(float) * y.nchunks * B * G * D);
   y.state = off;
-  if (op == PARARNN_OP_SOLVE && K >= 2) off = round_up(off + sizeof(float) * NS * B * L * D);
+  if (op == PARARNN_OP_SOLVE && K >= 2 && !fused) off = round_up(off + sizeof(float) * NS * B * L * D);
   y.total = off;
   return y;
 }
@@ -307,6 +341,33 @@ int scan(int ns, const float* A, const float* b, const float* s0, float* s, void
   return record(o, 2, stream);
 }
 
+bool use_fused(const pararnn_opts* o) {
+  return o->schedule == PARARNN_SCHEDULE_FUSED || (o->schedule == PARARNN_SCHEDULE_AUTO && !o->early_exit);
+}
+
+template <class Cell, class UT, int C>
+int launch_fused(const FusedArgs& a, hipStream_t s) {
+  using K = FusedCfg<Cell, C>;
+  const unsigned grid = static_cast<unsigned>(a.B) * a.ntiles_d * static_cast<unsigned>(a.nchunks);
+  const FusedArgs& b = a;
+  hipLaunchKernelGGL((newton_fused_kernel<Cell, UT, C, K::T, K::W, K::LL, K::OCC, K::UKEEP>), dim3(grid),
+                     dim3(64 * K::W), 0, s, b);
+  return check_hip(hipGetLastError());
+}
+
+template <class Cell, class UT>
+int launch_fused_c(int C, const FusedArgs& a, hipStream_t s) {
+  if constexpr (max_c<Cell, false>() >= 2) {
+    if (C == 2) return launch_fused<Cell, UT, 2>(a, s);
+  }
+  return launch_fused<Cell, UT, 1>(a, s);
+}
+
+template <class Cell>
+int launch_fused_any(int dtype, int C, const FusedArgs& a, hipStream_t s) {
+  return dtype == PARARNN_BF16 ? launch_fused_c<Cell, bf16>(C, a, s) : launch_fused_c<Cell, float>(C, a, s);
+}
+
 int solve(int cell, const void* u, const float* a, const float* c0, const float* h0, float* c, float* h,
           void* ws, size_t ws_bytes, const pararnn_opts* o, int32_t* iters, int32_t* converged,
           float* max_update, hipStream_t stream) {
@@ -317,14 +378,53 @@ int solve(int cell, const void* u, const float* a, const float* c0, const float*
   const size_t usize = o->u_dtype == PARARNN_BF16 ? 2 : 4;
   const int C = pick_c(cmax_for(cell, PARARNN_OP_SOLVE), o->D, usize, u, {a, h0, h, c0, c});
   if (!C || !aligned(u, usize)) return PARARNN_EUNSUPPORTED;
-  const Geo g = geo_for(cell, PARARNN_OP_SOLVE, C);
+  const bool fused = use_fused(o);
+  const Geo g = fused ? fused_geo_for(cell, C) : geo_for(cell, PARARNN_OP_SOLVE, C);
   // one chunk of gate inputs (and of states) is addressed with 32-bit offsets below 2^31
   if (static_cast<double>(g.chunk) * ngates(cell) * o->D * 4.0 >= 2147483648.0) return PARARNN_EUNSUPPORTED;
-  const Layout y = layout(cell, PARARNN_OP_SOLVE, o, false, g);
+  const Layout y = layout(cell, PARARNN_OP_SOLVE, o, false, g, fused);
   if (ws_bytes < y.total) return PARARNN_EWORKSPACE;
   if (!aligned(ws, kAlign)) return PARARNN_EUNSUPPORTED;
 
   const int K = o->max_iters, NS = nstate(cell);
+  if (fused) {
+    int rc = record(o, 0, stream);
+    if (rc) return rc;
+    rc = clear_ws(static_cast<char*>(ws), y, nullptr, 0, stream);
+    if (rc) return rc;
+    rc = record(o, 1, stream);
+    if (rc) return rc;
+    char* w = static_cast<char*>(ws);
+    FusedArgs fa;
+    memset(&fa, 0, sizeof(fa));
+    fa.u = u;
+    fa.a = a;
+    fa.s0[0] = cell == PARARNN_LSTM ? c0 : h0;
+    fa.s0[1] = cell == PARARNN_LSTM ? h0 : nullptr;
+    fa.sout[0] = cell == PARARNN_LSTM ? c : h;
+    fa.sout[1] = cell == PARARNN_LSTM ? h : nullptr;
+    fa.incl = reinterpret_cast<unsigned long long*>(w + y.incl);
+    fa.agg = reinterpret_cast<unsigned long long*>(w + y.agg);
+    fa.ctr = reinterpret_cast<unsigned int*>(w + y.ctr);
+    fa.pmax = reinterpret_cast<unsigned int*>(w + y.pmax);
+    fa.B = o->B;
+    fa.L = o->L;
+    fa.D = o->D;
+    fa.K = K;
+    fa.nchunks = y.nchunks;
+    fa.ntiles_d = y.ntiles_d;
+    rc = (cell == PARARNN_LSTM) ? launch_fused_any<LstmCell>(o->u_dtype, C, fa, stream)
+                                : launch_fused_any<GruCell>(o->u_dtype, C, fa, stream);
+    if (rc) return rc;
+    for (int k = 1; k <= K; ++k) {
+      rc = record(o, k + 1, stream);
+      if (rc) return rc;
+    }
+    hipLaunchKernelGGL(newton_finalize_kernel, dim3(o->B, K), dim3(kRowmaxThreads), 0, stream,
+                       static_cast<const unsigned int*>(fa.pmax), reinterpret_cast<unsigned int*>(w + y.maxupd),
+                       o->B, y.ntiles_d, y.nchunks, K, o->tol, 0, iters, converged, max_update);
+    return check_hip(hipGetLastError());
+  }
   const size_t BLD = static_cast<size_t>(o->B) * o->L * o->D;
   char* w = static_cast<char*>(ws);
   float* buf = reinterpret_cast<float*>(w + y.state);
@@ -390,9 +490,11 @@ using namespace pararnn;
 
 extern "C" size_t pararnn_workspace_bytes(int32_t cell, int32_t op, const pararnn_opts* o) {
   if (!opts_ok(cell, op, o)) return 0;
+  const bool fused = op == PARARNN_OP_SOLVE && use_fused(o);
   size_t n = 0;
   for (int C = 1; C <= cmax_for(cell, op); C *= 2) {
-    const size_t t = layout(cell, op, o, true, geo_for(cell, op, C)).total;
+    const Geo g = fused ? fused_geo_for(cell, C) : geo_for(cell, op, C);
+    const size_t t = layout(cell, op, o, true, g, fused).total;
     n = t > n ? t : n;
   }
   return n;

@@ -23,7 +23,7 @@ def dev():
     return torch.device("cuda:0")
 
 
-def gpu_solve(cell, x, iters=3, s0=None, tol=1e-4, early_exit=False, u=None, a=None):
+def gpu_solve(cell, x, iters=3, s0=None, tol=1e-4, early_exit=False, u=None, a=None, schedule="auto"):
     """Run the HIP solve on the inputs of x (u or a replaced when given); returns
     (states [NS][B][L][D] fp64, iters, conv, max_update)."""
     d = dev()
@@ -37,7 +37,7 @@ def gpu_solve(cell, x, iters=3, s0=None, tol=1e-4, early_exit=False, u=None, a=N
         else:
             kw["c0"] = s0t[0].contiguous().to(d)
             kw["h0"] = s0t[1].contiguous().to(d)
-    r = binding.solve(cell, ug, ag, iters=iters, tol=tol, early_exit=early_exit, **kw)
+    r = binding.solve(cell, ug, ag, iters=iters, tol=tol, early_exit=early_exit, schedule=schedule, **kw)
     torch.cuda.synchronize()
     st = [r["h"]] if cell == "gru" else [r["c"], r["h"]]
     S = np.stack([t.cpu().double().numpy() for t in st])

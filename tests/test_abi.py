@@ -37,18 +37,30 @@ def test_status_codes_match_header(lib):
 
 
 def test_opts_struct_layout():
-    assert ctypes.sizeof(b.Opts) == 40
+    assert ctypes.sizeof(b.Opts) == 48
     assert b.Opts.events.offset == 32
+    assert b.Opts.schedule.offset == 40
+
+
+def _ws(lib, cell, op, B, L, D, K, schedule="auto", early_exit=False):
+    o, _ = b.make_opts(B, L, D, K, 1e-4, early_exit, b.BF16, None, schedule)
+    return lib.pararnn_workspace_bytes(b.CELLS[cell], op, ctypes.byref(o))
 
 
 def test_workspace_bytes(lib):
-    # solve: counters, row maxima, descriptors, one ping-pong state buffer (K >= 2)
+    # per-iteration schedule: counters, row maxima, descriptors, one ping-pong
+    # state buffer (K >= 2)
     B, L, D = 8, 4096, 1024
-    n = b.workspace_bytes("gru", b.OP_SOLVE, B, L, D, 3)
+    n = _ws(lib, "gru", b.OP_SOLVE, B, L, D, 3, "per_iteration")
     assert n >= 4 * B * L * D
-    assert b.workspace_bytes("lstm", b.OP_SOLVE, B, L, D, 3) >= 8 * B * L * D
+    assert _ws(lib, "lstm", b.OP_SOLVE, B, L, D, 3, "per_iteration") >= 8 * B * L * D
     # K = 1 needs no state buffer
-    assert b.workspace_bytes("gru", b.OP_SOLVE, B, L, D, 1) < 4 * B * L * D
+    assert _ws(lib, "gru", b.OP_SOLVE, B, L, D, 1, "per_iteration") < 4 * B * L * D
+    # fused schedule (the default without early exit): no state buffer, one
+    # descriptor set per iteration
+    fused = _ws(lib, "gru", b.OP_SOLVE, B, L, D, 3)
+    assert fused == _ws(lib, "gru", b.OP_SOLVE, B, L, D, 3, "fused") and 0 < fused < 4 * B * L * D
+    assert _ws(lib, "gru", b.OP_SOLVE, B, L, D, 3, early_exit=True) == n  # early exit runs per iteration
     # single chunk: no descriptors
     assert b.workspace_bytes("gru", b.OP_SOLVE, 1, 100, 64, 1) <= 4096
     # invalid options -> 0
@@ -60,9 +72,10 @@ def test_workspace_bytes(lib):
     assert lib.pararnn_workspace_bytes(0, 0, None) == 0
 
 
-def _solve_status(lib, u=1, a=1, h=1, ws=1, ws_bytes=1 << 40, B=2, L=8, D=4, K=3, dtype=1, early=0):
+def _solve_status(lib, u=1, a=1, h=1, ws=1, ws_bytes=1 << 40, B=2, L=8, D=4, K=3, dtype=1, early=0, schedule=0):
     o, _ = b.make_opts(B, L, D, K, 1e-4, early, dtype)
     o.early_exit = early
+    o.schedule = schedule
     P = lambda v: ctypes.c_void_p(v * 4096) if v else None  # noqa: E731  (never dereferenced)
     return lib.pararnn_solve_gru(P(u), P(a), None, P(h), P(ws), ws_bytes, ctypes.byref(o), None, None,
                                  None, None)
@@ -78,6 +91,8 @@ def test_invalid_arguments_rejected_before_launch(lib):
     assert _solve_status(lib, D=0) == -1
     assert _solve_status(lib, K=0) == -1
     assert _solve_status(lib, early=2) == -1
+    assert _solve_status(lib, schedule=3) == -1 and _solve_status(lib, schedule=-1) == -1
+    assert _solve_status(lib, schedule=1, early=1) == -1  # the fused schedule has no early exit
     assert _solve_status(lib, dtype=5) == -2
     assert _solve_status(lib, ws_bytes=16) == -3
     o, _ = b.make_opts(2, 8, 4, 3)

@@ -61,12 +61,14 @@ def test_scan_nan_propagates_along_its_channel(ns):
 
 
 @pytest.mark.parametrize("ns", [1, 2])
-def test_scan_deterministic_and_workspace_reuse(ns):
+def test_scan_repeat_and_workspace_reuse(ns):
+    """Same inputs, same workspace: equal to rounding (the look-back's
+    association may vary from run to run)."""
     x = make_scan_inputs(ns, 2, 3000, 256, seed=53)
     r1 = _run(x, True)
     s1 = r1["s"].clone()
     r2 = _run(x, True, ws=r1["ws"])
-    assert torch.equal(s1, r2["s"])
+    assert float((s1 - r2["s"]).abs().max()) <= 1e-5
 
 
 @pytest.mark.parametrize("ns", [1, 2])

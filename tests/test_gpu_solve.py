@@ -22,38 +22,41 @@ SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("schedule", ["fused", "per_iteration"])
 @pytest.mark.parametrize("cell", ["gru", "lstm"])
 @pytest.mark.parametrize("u_dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("B,L,D", SHAPES, ids=[f"{b}x{l}x{d}" for b, l, d in SHAPES])
-def test_solve_matches_oracle(cell, u_dtype, B, L, D):
-    say(f"solve {cell} {u_dtype} B={B} L={L} D={D}")
+def test_solve_matches_oracle(cell, u_dtype, B, L, D, schedule):
+    say(f"solve {cell} {u_dtype} B={B} L={L} D={D} {schedule}")
     x = make_inputs(cell, B, L, D, seed=1000 + B * 7 + L * 3 + D, u_dtype=u_dtype)
-    S, iters, conv, mu = gpu_solve(cell, x, iters=3)
+    S, iters, conv, mu = gpu_solve(cell, x, iters=3, schedule=schedule)
     want, upd = O.newton(cell, x.u, x.a, K=3)
     assert_close(S, want, STATE_TOL, f"{cell} state")
     assert_close(mu, upd, 1e-4, "max_update")
     check_flags(iters, conv, upd, 3, 1e-4)
 
 
+@pytest.mark.parametrize("schedule", ["fused", "per_iteration"])
 @pytest.mark.parametrize("cell", ["gru", "lstm"])
 @pytest.mark.parametrize("K", [1, 2, 4])
-def test_iteration_counts(cell, K):
-    say(f"solve {cell} K={K}")
+def test_iteration_counts(cell, K, schedule):
+    say(f"solve {cell} K={K} {schedule}")
     x = make_inputs(cell, 2, 700, 96, seed=77 + K, u_dtype="bf16")
-    S, iters, conv, mu = gpu_solve(cell, x, iters=K)
+    S, iters, conv, mu = gpu_solve(cell, x, iters=K, schedule=schedule)
     want, upd = O.newton(cell, x.u, x.a, K=K)
     assert_close(S, want, STATE_TOL, f"{cell} K={K}")
     check_flags(iters, conv, upd, K, 1e-4)
 
 
+@pytest.mark.parametrize("schedule", ["fused", "per_iteration"])
 @pytest.mark.parametrize("cell", ["gru", "lstm"])
-def test_initial_state(cell):
-    say(f"solve {cell} with initial state")
+def test_initial_state(cell, schedule):
+    say(f"solve {cell} with initial state, {schedule}")
     B, L, D = 3, 400, 68
     x = make_inputs(cell, B, L, D, seed=5, u_dtype="bf16")
     NS = 2 if cell == "lstm" else 1
     s0 = np.random.default_rng(0).normal(size=(NS, B, D)).astype(np.float32)
-    S, iters, conv, mu = gpu_solve(cell, x, iters=3, s0=s0)
+    S, iters, conv, mu = gpu_solve(cell, x, iters=3, s0=s0, schedule=schedule)
     want, upd = O.newton(cell, x.u, x.a, K=3, s0=s0_float32(s0))
     assert_close(S, want, STATE_TOL, f"{cell} with s0")
 
@@ -117,9 +120,10 @@ def test_nan_input_propagates():
     assert_close(S[:, ok], want[:, ok], STATE_TOL, "rows without NaN")
 
 
+@pytest.mark.parametrize("schedule", ["fused", "per_iteration"])
 @pytest.mark.parametrize("cell", ["gru", "lstm"])
 @pytest.mark.parametrize("with_s0", [False, True], ids=["s0_zero", "s0_given"])
-def test_nonfinite_coefficient_propagates(cell, with_s0):
+def test_nonfinite_coefficient_propagates(cell, with_s0, schedule):
     """Non-finite coefficients (inf in one channel, NaN in another) give the
     oracle's NaN pattern: a * 0 at the zero starting iterate is NaN, so the
     channel turns NaN from its first step at that iterate on, while the first
@@ -134,7 +138,7 @@ def test_nonfinite_coefficient_propagates(cell, with_s0):
     a[2, 9] = float("nan")
     NS = 2 if cell == "lstm" else 1
     s0 = np.random.default_rng(3).normal(size=(NS, B, D)).astype(np.float32) if with_s0 else None
-    S, iters, conv, mu = gpu_solve(cell, x, iters=3, a=a, s0=s0)
+    S, iters, conv, mu = gpu_solve(cell, x, iters=3, a=a, s0=s0, schedule=schedule)
     want, upd = O.newton(cell, x.u, a, K=3, s0=s0_float32(s0))
     assert np.isnan(want[..., 1:, 5]).all() and np.isnan(want[..., 1:, 9]).all()
     assert np.array_equal(np.isnan(S), np.isnan(want)), "NaN pattern differs from the oracle's"
@@ -143,19 +147,25 @@ def test_nonfinite_coefficient_propagates(cell, with_s0):
     assert np.isnan(mu).all() and not conv.any() and iters == 3
 
 
+@pytest.mark.parametrize("schedule", ["fused", "per_iteration"])
 @pytest.mark.parametrize("cell", ["gru", "lstm"])
-def test_deterministic_and_workspace_reuse(cell):
-    say(f"solve {cell} determinism")
+def test_repeat_and_workspace_reuse(cell, schedule):
+    """A second solve in the same workspace reproduces the first. The
+    cross-chunk carry composes whichever predecessor values the decoupled
+    look-back finds published, so the fp32 association (not the result beyond
+    rounding) may differ from run to run: equal to 1e-6, not bit for bit."""
+    say(f"solve {cell} repeat, {schedule}")
     x = make_inputs(cell, 2, 3000, 256, seed=29, u_dtype="bf16")
     d = torch.device("cuda:0")
     u, a = x.u.to(d), x.a.to(d)
-    r1 = binding.solve(cell, u, a)
+    r1 = binding.solve(cell, u, a, schedule=schedule)
     h1 = r1["h"].clone()
-    r2 = binding.solve(cell, u, a, ws=r1["ws"])
+    c1 = r1["c"].clone() if cell == "lstm" else None
+    r2 = binding.solve(cell, u, a, ws=r1["ws"], schedule=schedule)
     torch.cuda.synchronize()
-    assert torch.equal(h1, r2["h"])
+    assert float((h1 - r2["h"]).abs().max()) <= 1e-6
     if cell == "lstm":
-        assert torch.equal(r1["c"], r2["c"])
+        assert float((c1 - r2["c"]).abs().max()) <= 1e-6
 
 
 @pytest.mark.parametrize("cell", ["gru", "lstm"])

@@ -30,15 +30,16 @@ def _sampled(t, chans, D):
     return t[b, :, d].T.cpu().double().numpy()
 
 
+@pytest.mark.parametrize("schedule", ["fused", "per_iteration"])
 @pytest.mark.parametrize("name", list(WORKLOADS))
-def test_workload_parity(name):
+def test_workload_parity(name, schedule):
     w = WORKLOADS[name]
-    say(f"workload {name}: generating inputs")
+    say(f"workload {name} ({schedule}): generating inputs")
     x = workload_inputs(w)
     dev = torch.device("cuda:0")
     u, a = x.u.to(dev), x.a.to(dev)
     say(f"workload {name}: solve")
-    r = binding.solve(w.cell, u, a, iters=w.iters)
+    r = binding.solve(w.cell, u, a, iters=w.iters, schedule=schedule)
     torch.cuda.synchronize()
     chans = sample_channels(w.B, w.D, NSAMPLE, seed=7)
     us = gather_channels(x.u, chans, w.D)
@@ -99,4 +100,4 @@ def test_workload_parity(name):
         assert_close(da_got, da_want, 1e-4 * scale, f"{name} da at sampled channels")
         ds0_got = g2["ds0"][:, :, dsel].permute(0, 2, 1).reshape(ds0_want.shape[0], 1, -1).cpu().double().numpy()
         assert_close(ds0_got, ds0_want, 1e-4, f"{name} ds0 at sampled channels")
-        assert torch.equal(g2["du"], g["du"])  # requesting da and ds0 leaves du unchanged
+        assert float((g2["du"] - g["du"]).abs().max()) <= 1e-6  # requesting da and ds0 leaves du as it was
