@@ -45,7 +45,9 @@ def _bind(path):
     lib.oracle_adjoint.argtypes = [I, I, I, I, P, P, P, P, P, P, P, P, I]
     lib.oracle_cell.argtypes = [I, I, P, P, P, P, P, P, P]
     lib.oracle_scan.argtypes = [I, I, I, I, P, P, P, P, I]
-    for f in (lib.oracle_seq, lib.oracle_newton, lib.oracle_adjoint, lib.oracle_cell, lib.oracle_scan):
+    lib.oracle_scan_dense.argtypes = [I, I, I, P, P, P, P, I]
+    for f in (lib.oracle_seq, lib.oracle_newton, lib.oracle_adjoint, lib.oracle_cell, lib.oracle_scan,
+              lib.oracle_scan_dense):
         f.restype = I
     return lib
 
@@ -217,6 +219,25 @@ def scan(A, b, s0=None, nthreads=None):
     rc = _load().oracle_scan(ns, B, L, D, _ptr(A), _ptr(b), _ptr(s0), _ptr(s), nthreads or default_threads())
     if rc:
         raise ValueError(f"oracle_scan failed ({rc})")
+    return s
+
+
+def scan_dense(A, b, s0=None, nthreads=None):
+    """Linear recurrence with a dense n x n matrix per step: A [B][L][n][n]
+    (A_l[r][q] multiplies s_{l-1}[q] into s_l[r]), b [B][L][n], s0 [B][n] or
+    None. Returns s [B][L][n] (fp64)."""
+    A = _np(A, np.float64)
+    b = _np(b, np.float64)
+    if A.ndim != 4 or A.shape[2] != A.shape[3] or b.shape != A.shape[:3]:
+        raise ValueError("A must be [B][L][n][n] and b [B][L][n]")
+    B, L, n = b.shape
+    s0 = _np(s0, np.float64)
+    if s0 is not None and s0.shape != (B, n):
+        raise ValueError("s0 must be [B][n]")
+    s = np.empty(b.shape, np.float64)
+    rc = _load().oracle_scan_dense(B, L, n, _ptr(A), _ptr(b), _ptr(s0), _ptr(s), nthreads or default_threads())
+    if rc:
+        raise ValueError(f"oracle_scan_dense failed ({rc})")
     return s
 
 

@@ -503,3 +503,50 @@ int oracle_scan(int ns, int B, int L, int D, const double* A, const double* b, c
   parallel_over_d(D, nthreads, scan_worker, &c);
   return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* O5. The linear recurrence with a dense n x n matrix per step: the          */
+/* linearised system of a generic RNN, whose Jacobians are dense (ParaRNN     */
+/* article, cafecomtech.com, section "Engenharia pra escalar": storage grows  */
+/* as n^2 and the products as n^3):                                          */
+/*   s_l = A_l s_{l-1} + b_l,  l = 0 .. L-1,  s_{-1} = s0 (zero when NULL).   */
+/* Layouts (row-major): A [B][L][n][n] (A_l[r][q] multiplies s_{l-1}[q] into */
+/* s_l[r]), b and s [B][L][n], s0 [B][n]. Threads split the batch rows.      */
+typedef struct {
+  int B, L, n;
+  const double *A, *b, *s0;
+  double* s;
+} dense_ctx;
+
+static void dense_worker(void* vctx, int b_lo, int b_hi) {
+  const dense_ctx* c = (const dense_ctx*)vctx;
+  const int n = c->n;
+  double* prev = (double*)malloc(sizeof(double) * (size_t)n);
+  double* next = (double*)malloc(sizeof(double) * (size_t)n);
+  for (int b = b_lo; b < b_hi; ++b) {
+    for (int r = 0; r < n; ++r) prev[r] = c->s0 ? c->s0[(size_t)b * n + r] : 0.0;
+    for (int l = 0; l < c->L; ++l) {
+      const size_t step = (size_t)b * c->L + l;
+      const double* Al = c->A + step * n * n;
+      for (int r = 0; r < n; ++r) {
+        double acc = c->b[step * n + r];
+        for (int q = 0; q < n; ++q) acc += Al[(size_t)r * n + q] * prev[q];
+        next[r] = acc;
+      }
+      for (int r = 0; r < n; ++r) {
+        c->s[step * n + r] = next[r];
+        prev[r] = next[r];
+      }
+    }
+  }
+  free(prev);
+  free(next);
+}
+
+int oracle_scan_dense(int B, int L, int n, const double* A, const double* b, const double* s0, double* s,
+                      int nthreads) {
+  if (B <= 0 || L <= 0 || n <= 0 || !A || !b || !s) return -1;
+  dense_ctx c = {B, L, n, A, b, s0, s};
+  parallel_over_d(B, nthreads, dense_worker, &c);
+  return 0;
+}

@@ -40,6 +40,12 @@ MUTANTS = [
     ("scan_initial_state_ignored", "prev[r] = c->s0 ? c->s0[((size_t)r * c->B + b) * c->D + d] : 0.0;",
      "prev[r] = 0.0;"),
     ("scan_state_not_advanced", "          prev[r] = next[r];\n", "\n"),
+    ("dense_transposed", "for (int q = 0; q < n; ++q) acc += Al[(size_t)r * n + q] * prev[q];",
+     "for (int q = 0; q < n; ++q) acc += Al[(size_t)q * n + r] * prev[q];"),
+    ("dense_initial_state_ignored", "for (int r = 0; r < n; ++r) prev[r] = c->s0 ? c->s0[(size_t)b * n + r] : 0.0;",
+     "for (int r = 0; r < n; ++r) prev[r] = 0.0;"),
+    ("dense_input_dropped_first_step", "double acc = c->b[step * n + r];",
+     "double acc = l ? c->b[step * n + r] : 0.0;"),
 ]
 
 
@@ -68,6 +74,9 @@ def _pins():
         ("scan_rotation", lambda: P.test_scan_block_rotation_closed_form(O)),
         ("scan_dense_1", lambda: P.test_scan_dense_bidiagonal_solve(O, 1)),
         ("scan_dense_2", lambda: P.test_scan_dense_bidiagonal_solve(O, 2)),
+        ("dense_shift", lambda: P.test_dense_recurrence_cyclic_shift_closed_form(O)),
+        ("dense_geometric", lambda: P.test_dense_recurrence_scaled_identity_geometric(O)),
+        ("dense_solve", lambda: P.test_dense_recurrence_bidiagonal_solve(O)),
     ]
     pins.append(("gru_closed_form", lambda: P.test_gru_linear_cell_closed_form(O)))
     pins.append(("lstm_closed_form", lambda: P.test_lstm_linear_cell_closed_form(O)))

@@ -526,3 +526,58 @@ def test_scan_is_linear_in_inputs_and_initial_state(oracle_lib):
     lhs = oracle_lib.scan(A, b1 + 2.0 * b2, s1 - s2)
     rhs = oracle_lib.scan(A, b1, s1) + 2.0 * oracle_lib.scan(A, b2, None) - oracle_lib.scan(A, 0 * b1, s2)
     np.testing.assert_allclose(lhs, rhs, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# The dense recurrence (O5): s_l = A_l s_{l-1} + b_l with an n x n matrix.
+
+def test_dense_recurrence_cyclic_shift_closed_form(oracle_lib):
+    """A = cyclic shift (A[r][r-1 mod n] = 1), b = 0: s_l = s0 shifted by l+1
+    positions towards higher indices. The transposed matrix shifts the other way."""
+    n, L = 5, 12
+    P = np.zeros((n, n))
+    for r in range(n):
+        P[r, (r - 1) % n] = 1.0
+    A = np.broadcast_to(P, (1, L, n, n))
+    s0 = np.arange(1.0, n + 1.0)[None]
+    s = oracle_lib.scan_dense(A, np.zeros((1, L, n)), s0)
+    for l in range(L):
+        np.testing.assert_array_equal(s[0, l], np.roll(s0[0], l + 1))
+
+
+def test_dense_recurrence_scaled_identity_geometric(oracle_lib):
+    """A = alpha I, b = beta: each component is the scalar geometric closed form."""
+    n, L, alpha = 4, 40, 0.9
+    beta = np.array([1.0, -2.0, 0.5, 3.0])
+    s0 = np.array([[0.2, -1.0, 4.0, 0.0]])
+    A = np.broadcast_to(alpha * np.eye(n), (1, L, n, n))
+    s = oracle_lib.scan_dense(A, np.broadcast_to(beta, (1, L, n)), s0)
+    p = alpha ** np.arange(1, L + 1)[:, None]
+    np.testing.assert_allclose(s[0], p * s0[0] + beta * (1 - p) / (1 - alpha), rtol=1e-12, atol=1e-12)
+
+
+def test_dense_recurrence_bidiagonal_solve(oracle_lib):
+    """The recurrence as one block lower-bidiagonal system, numpy.linalg.solve."""
+    rng = np.random.default_rng(60)
+    L, n = 6, 4
+    A = rng.normal(size=(L, n, n))
+    b = rng.normal(size=(L, n))
+    s0 = rng.normal(size=n)
+    M = np.eye(L * n)
+    for l in range(1, L):
+        M[l * n:(l + 1) * n, (l - 1) * n:l * n] = -A[l]
+    rhs = b.reshape(-1).copy()
+    rhs[:n] += A[0] @ s0
+    want = np.linalg.solve(M, rhs).reshape(L, n)
+    got = oracle_lib.scan_dense(A[None], b[None], s0[None])[0]
+    np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-10)
+
+
+def test_dense_recurrence_linear_in_inputs(oracle_lib):
+    rng = np.random.default_rng(61)
+    A = rng.normal(size=(2, 25, 3, 3)) * 0.5
+    b1, b2 = rng.normal(size=(2, 2, 25, 3))
+    s1, s2 = rng.normal(size=(2, 2, 3))
+    lhs = oracle_lib.scan_dense(A, b1 - 3.0 * b2, s1 + s2)
+    rhs = oracle_lib.scan_dense(A, b1, s1) - 3.0 * oracle_lib.scan_dense(A, b2) + oracle_lib.scan_dense(A, 0 * b1, s2)
+    np.testing.assert_allclose(lhs, rhs, rtol=1e-11, atol=1e-11)
