@@ -30,6 +30,7 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak
 # lane-operations per second (the fp32 vector 157.3 TFLOP/s counts a packed
 # FMA, 4 flops, per lane-operation)
 PEAK_VALU_TSLOTS = 256 * 64 * 2.4e9 / 1e12
+PEAK_F32_MATRIX_TFLOPS = 157.3  # MI355X dense fp32 matrix-core peak
 
 
 # VALU issue slots per state element per Newton iteration (cell, Jacobian,
@@ -227,6 +228,68 @@ def cpu_baseline_scan(w, x, target_s=12.0):
             "sample": f"{nb} of {w.B} batch rows (all D={w.D}, full L={w.L}), fp64 loop; {t:.2f} s"}
 
 
+def bench_scan_dense(w, args):
+    """The dense recurrence (pararnn_scan_dense): chunk transfers on the matrix
+    cores, carries, then the recurrence per chunk."""
+    import torch
+    from nonlinear_rnn_solve_newton_amd import binding
+    from nonlinear_rnn_solve_newton_amd.workloads import dense_workload_inputs
+
+    dev = torch.device("cuda:0")
+    x = dense_workload_inputs(w)
+    A, b, s0 = x.A.to(dev), x.b.to(dev), x.s0.to(dev)
+    hip = HipEvents()
+    ev = hip.create(3)
+    first = binding.scan_dense(A, b, s0)
+    ws, out = first["ws"], first["s"]
+    for _ in range(args.warmup):
+        binding.scan_dense(A, b, s0, out=out, ws=ws)
+    torch.cuda.synchronize()
+    kms = []
+    for _ in range(args.steps):
+        binding.scan_dense(A, b, s0, out=out, ws=ws, events=ev)
+        kms.append(hip.ms(ev[1], ev[2]))
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        binding.scan_dense(A, b, s0, out=out, ws=ws)
+    stop.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    t = sum(kms) / len(kms)
+    steps = w.B * w.L
+    nbytes = steps * (w.n * w.n + 2 * w.n) * 4  # read A and b once, write s once
+    flops = steps * 2 * 32 ** 3  # one 32x32x32 transfer product per step (fp32 matrix cores)
+    achieved = nbytes / (t * 1e-3) / 1e9
+    result = {
+        "metric": "scanned state elems/s (B*L*n) of the dense recurrence s_l = A_l s_{l-1} + b_l",
+        "value": w.N / (ms_step * 1e-3), "unit": "elems/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded; A = 0.95 x random orthogonal, b, s0 ~ N(0,1))",
+        "config": {"workload": w.name, "B": w.B, "L": w.L, "n": w.n},
+        "roofline": {"bound": "hbm", "kernel": "dense_chunk_kernel + dense_carry_kernel + dense_segcarry_kernel + dense_apply_kernel",
+                     "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": None, "algorithmic_bytes_per_launch": [nbytes], "launch_ms": [t]},
+        "matrix_cores": {"achieved": flops / (t * 1e-3) / 1e12, "peak": PEAK_F32_MATRIX_TFLOPS,
+                         "unit": "TFLOP/s", "frac": flops / (t * 1e-3) / 1e12 / PEAK_F32_MATRIX_TFLOPS},
+        "timing": {"scan_ms": t, "source_digest": source_digest()},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import oracle as O
+        nthreads = O.default_threads()
+        t0 = time.perf_counter()
+        O.scan_dense(x.A, x.b, x.s0, nthreads=nthreads)
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": w.N / dt, "unit": "elems/s", "cores": min(nthreads, w.B),
+                                  "kind": "oracle",
+                                  "sample": f"the whole workload ({w.B} rows), fp64 loop; {dt:.2f} s"}
+    hip.destroy(ev)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def bench_scan(w, args):
     """The linear scan alone (pararnn_scan_diag / pararnn_scan_block2)."""
     import torch
@@ -350,11 +413,11 @@ def main(argv=None):
                     help="write profiles/<workload>_kernel_stats.md from a rocprofv3 --stats CSV")
     args = ap.parse_args(argv)
     sys.path.insert(0, str(ROOT))
-    from nonlinear_rnn_solve_newton_amd.workloads import HEADLINE, SCAN_WORKLOADS, WORKLOADS
+    from nonlinear_rnn_solve_newton_amd.workloads import DENSE_WORKLOADS, HEADLINE, SCAN_WORKLOADS, WORKLOADS
     name = args.workload or HEADLINE
-    if name not in WORKLOADS and name not in SCAN_WORKLOADS:
+    if name not in WORKLOADS and name not in SCAN_WORKLOADS and name not in DENSE_WORKLOADS:
         print(json.dumps({"error": f"unknown workload {name}",
-                          "workloads": sorted(WORKLOADS) + sorted(SCAN_WORKLOADS)}))
+                          "workloads": sorted(WORKLOADS) + sorted(SCAN_WORKLOADS) + sorted(DENSE_WORKLOADS)}))
         return 2
     if args.stats_summary:
         print(write_stats_summary(name, args.stats_summary))
@@ -378,6 +441,8 @@ def main(argv=None):
 
     if name in SCAN_WORKLOADS:
         return bench_scan(SCAN_WORKLOADS[name], args)
+    if name in DENSE_WORKLOADS:
+        return bench_scan_dense(DENSE_WORKLOADS[name], args)
     if args.generic:
         return bench_generic(WORKLOADS[name], args)
 

@@ -71,7 +71,8 @@ typedef enum {
   PARARNN_OP_SOLVE = 0,
   PARARNN_OP_ADJOINT = 1,
   PARARNN_OP_SCAN_DIAG = 2,   /* pararnn_scan_diag; the cell argument is ignored */
-  PARARNN_OP_SCAN_BLOCK2 = 3  /* pararnn_scan_block2; the cell argument is ignored */
+  PARARNN_OP_SCAN_BLOCK2 = 3, /* pararnn_scan_block2; the cell argument is ignored */
+  PARARNN_OP_SCAN_DENSE = 4   /* pararnn_scan_dense; the cell argument is ignored */
 } pararnn_op;
 
 typedef struct {
@@ -152,6 +153,21 @@ int32_t pararnn_scan_diag(const float* A, const float* b, const float* s0, float
                           size_t ws_bytes, const pararnn_opts* o, void* stream);
 int32_t pararnn_scan_block2(const float* A, const float* b, const float* s0, float* s, void* ws,
                             size_t ws_bytes, const pararnn_opts* o, void* stream);
+
+/* The linear scan with a dense n x n matrix per step: the linearised system of
+ * a generic RNN, whose Jacobians are dense (ParaRNN article, cafecomtech.com,
+ * section "Engenharia pra escalar": n^2 storage and n^3 products, hence small
+ * n only). Per batch row b, for l = 0 .. L-1:
+ *   s_l = A_l s_{l-1} + b_l,   s_{-1} = s0 (zero when s0 is NULL),
+ *   s_l[r] = sum_q A_l[r][q] s_{l-1}[q] + b_l[r].
+ * Layouts (device, fp32, row-major): A [B][L][n][n], b and s (output)
+ * [B][L][n], s0 [B][n] or NULL. n = opts.D, 1 <= n <= 32; opts.B and opts.L
+ * as usual; opts.events: 3 handles (before, after set-up, after the scan).
+ * The chunk transfer products run on the matrix cores in fp32. Workspace:
+ * pararnn_workspace_bytes(any cell, PARARNN_OP_SCAN_DENSE, o). Pointers need
+ * 4-byte alignment. Errors as for the other calls; n > 32 is EINVAL. */
+int32_t pararnn_scan_dense(const float* A, const float* b, const float* s0, float* s, void* ws,
+                           size_t ws_bytes, const pararnn_opts* o, void* stream);
 
 /* Static description of a status code. */
 const char* pararnn_strerror(int32_t status);

@@ -20,7 +20,7 @@ LIB_PATH = PKG / "libpararnn.so"
 HEADER = PKG.parent / "include" / "pararnn.h"
 
 GRU, LSTM = 0, 1
-OP_SOLVE, OP_ADJOINT, OP_SCAN_DIAG, OP_SCAN_BLOCK2 = 0, 1, 2, 3
+OP_SOLVE, OP_ADJOINT, OP_SCAN_DIAG, OP_SCAN_BLOCK2, OP_SCAN_DENSE = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
 CELLS = {"gru": GRU, "lstm": LSTM}
 GATES = {"gru": 3, "lstm": 4}
@@ -77,6 +77,8 @@ def lib():
         L.pararnn_scan_diag.restype = I32
         L.pararnn_scan_block2.argtypes = [P, P, P, P, P, SZ, OPTP, P]
         L.pararnn_scan_block2.restype = I32
+        L.pararnn_scan_dense.argtypes = [P, P, P, P, P, SZ, OPTP, P]
+        L.pararnn_scan_dense.restype = I32
         L.pararnn_strerror.argtypes = [I32]
         L.pararnn_strerror.restype = ctypes.c_char_p
         _lib = L
@@ -265,4 +267,32 @@ def scan(A: torch.Tensor, b: torch.Tensor, s0: Optional[torch.Tensor] = None, *,
     st = fn(_ptr(A), _ptr(b), _ptr(s0), _ptr(out), _ptr(ws), ws.numel(), ctypes.byref(o), _stream(A.device))
     del keep
     _check(st, "pararnn_scan_diag" if ns == 1 else "pararnn_scan_block2")
+    return dict(s=out, ws=ws)
+
+
+def scan_dense(A: torch.Tensor, b: torch.Tensor, s0: Optional[torch.Tensor] = None, *,
+               out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+               events: Optional[Sequence[int]] = None):
+    """Linear recurrence with a dense n x n matrix per step (pararnn_scan_dense):
+    A [B][L][n][n] (A_l[r][q] multiplies s_{l-1}[q] into s_l[r]), b [B][L][n],
+    s0 [B][n] or None; fp32 device tensors, n <= 32. Returns dict(s, ws)."""
+    _dev(A, "A", torch.float32)
+    if A.dim() != 4 or A.shape[2] != A.shape[3]:
+        raise PararnnError("A must be [B][L][n][n]")
+    B, L, n = A.shape[:3]
+    _dev(b, "b", torch.float32, (B, L, n))
+    _dev(s0, "s0", torch.float32, (B, n))
+    if out is None:
+        out = torch.empty(B, L, n, dtype=torch.float32, device=A.device)
+    _dev(out, "out", torch.float32, (B, L, n))
+    o, keep = make_opts(B, L, n, 1, 0.0, False, F32, events)
+    need = int(lib().pararnn_workspace_bytes(GRU, OP_SCAN_DENSE, ctypes.byref(o)))
+    if need == 0:
+        raise PararnnError("invalid sizes (the dense scan takes 1 <= n <= 32)")
+    if ws is None:
+        ws = alloc_workspace(need, A.device)
+    st = lib().pararnn_scan_dense(_ptr(A), _ptr(b), _ptr(s0), _ptr(out), _ptr(ws), ws.numel(), ctypes.byref(o),
+                                  _stream(A.device))
+    del keep
+    _check(st, "pararnn_scan_dense")
     return dict(s=out, ws=ws)

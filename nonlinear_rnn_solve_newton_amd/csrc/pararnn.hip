@@ -11,6 +11,7 @@
 #include "newton_fused.h"
 #include "newton_iter.h"
 #include "scan.h"
+#include "scan_dense.h"
 
 namespace pararnn {
 namespace {
@@ -147,6 +148,9 @@ int ngates(int cell) { return cell == PARARNN_LSTM ? 4 : 3; }
 
 bool opts_ok(int cell, int op, const pararnn_opts* o) {
   if (!o) return false;
+  if (op == PARARNN_OP_SCAN_DENSE)  // the dense scan has no cell; D is the state size
+    return o->B >= 1 && o->L >= 1 && o->D >= 1 && o->D <= kDenseMaxN &&
+           static_cast<double>(o->B) * ((o->L + kDenseChunk - 1) / kDenseChunk) < 2.0e9;
   if (op != PARARNN_OP_SOLVE && op != PARARNN_OP_ADJOINT && !is_scan(op)) return false;
   if (!is_scan(op) && cell != PARARNN_GRU && cell != PARARNN_LSTM) return false;  // the scan has no cell
   if (o->B < 1 || o->L < 1 || o->D < 1) return false;
@@ -483,6 +487,79 @@ int solve(int cell, const void* u, const float* a, const float* c0, const float*
   return check_hip(hipGetLastError());
 }
 
+// Dense scan workspace: chunk transfers [B][nchunks][32][32], local solutions
+// and carries [B][nchunks][32] each (nothing to clear: every entry is written
+// before it is read)
+struct DenseLayout {
+  size_t P = 0, v = 0, carry = 0, Pseg = 0, vseg = 0, cseg = 0, total = 0;
+  int nchunks = 0;
+};
+
+DenseLayout dense_layout(const pararnn_opts* o) {
+  DenseLayout y;
+  y.nchunks = (o->L + kDenseChunk - 1) / kDenseChunk;
+  const size_t nc = static_cast<size_t>(o->B) * y.nchunks, ns = nc * kDenseWaves;
+  y.P = 0;
+  y.v = round_up(sizeof(float) * nc * 1024);
+  y.carry = round_up(y.v + sizeof(float) * nc * 32);
+  y.Pseg = round_up(y.carry + sizeof(float) * nc * 32);
+  y.vseg = round_up(y.Pseg + sizeof(float) * ns * 1024);
+  y.cseg = round_up(y.vseg + sizeof(float) * ns * 32);
+  y.total = round_up(y.cseg + sizeof(float) * ns * 32);
+  return y;
+}
+
+int scan_dense(const float* A, const float* b, const float* s0, float* s, void* ws, size_t ws_bytes,
+               const pararnn_opts* o, hipStream_t stream) {
+  if (!opts_ok(PARARNN_GRU, PARARNN_OP_SCAN_DENSE, o)) return PARARNN_EINVAL;
+  if (!A || !b || !s || !ws) return PARARNN_EINVAL;
+  for (const void* q : {static_cast<const void*>(A), static_cast<const void*>(b), static_cast<const void*>(s0),
+                        static_cast<const void*>(s)})
+    if (q && !aligned(q, sizeof(float))) return PARARNN_EUNSUPPORTED;
+  const DenseLayout y = dense_layout(o);
+  if (ws_bytes < y.total) return PARARNN_EWORKSPACE;
+  if (!aligned(ws, kAlign)) return PARARNN_EUNSUPPORTED;
+  char* w = static_cast<char*>(ws);
+  DenseArgs da;
+  da.A = A;
+  da.b = b;
+  da.s0 = s0;
+  da.s = s;
+  da.P = reinterpret_cast<float*>(w + y.P);
+  da.v = reinterpret_cast<float*>(w + y.v);
+  da.carry = reinterpret_cast<float*>(w + y.carry);
+  da.Pseg = reinterpret_cast<float*>(w + y.Pseg);
+  da.vseg = reinterpret_cast<float*>(w + y.vseg);
+  da.cseg = reinterpret_cast<float*>(w + y.cseg);
+  da.B = o->B;
+  da.L = o->L;
+  da.n = o->D;
+  da.nchunks = y.nchunks;
+  const unsigned nwg = static_cast<unsigned>(o->B) * static_cast<unsigned>(y.nchunks);
+  int rc = record(o, 0, stream);
+  if (rc) return rc;
+  rc = record(o, 1, stream);
+  if (rc) return rc;
+  // n = 32 with 16-byte aligned A reads whole runs of four columns
+  const bool n32 = o->D == 32 && aligned(A, 16);
+  if (n32) hipLaunchKernelGGL(dense_chunk_kernel<true>, dim3(nwg), dim3(64 * kDenseWaves), 0, stream, da);
+  else hipLaunchKernelGGL(dense_chunk_kernel<false>, dim3(nwg), dim3(64 * kDenseWaves), 0, stream, da);
+  rc = check_hip(hipGetLastError());
+  if (rc) return rc;
+  hipLaunchKernelGGL(dense_carry_kernel, dim3(static_cast<unsigned>(o->B)), dim3(64), 0, stream, da);
+  rc = check_hip(hipGetLastError());
+  if (rc) return rc;
+  hipLaunchKernelGGL(dense_segcarry_kernel, dim3(nwg), dim3(64), 0, stream, da);
+  rc = check_hip(hipGetLastError());
+  if (rc) return rc;
+  const unsigned nseg = nwg * kDenseWaves;
+  if (n32) hipLaunchKernelGGL(dense_apply_kernel<true>, dim3(nseg), dim3(64), 0, stream, da);
+  else hipLaunchKernelGGL(dense_apply_kernel<false>, dim3(nseg), dim3(64), 0, stream, da);
+  rc = check_hip(hipGetLastError());
+  if (rc) return rc;
+  return record(o, 2, stream);
+}
+
 }  // namespace
 }  // namespace pararnn
 
@@ -490,6 +567,7 @@ using namespace pararnn;
 
 extern "C" size_t pararnn_workspace_bytes(int32_t cell, int32_t op, const pararnn_opts* o) {
   if (!opts_ok(cell, op, o)) return 0;
+  if (op == PARARNN_OP_SCAN_DENSE) return dense_layout(o).total;
   const bool fused = op == PARARNN_OP_SOLVE && use_fused(o);
   size_t n = 0;
   for (int C = 1; C <= cmax_for(cell, op); C *= 2) {
@@ -503,6 +581,11 @@ extern "C" size_t pararnn_workspace_bytes(int32_t cell, int32_t op, const pararn
 extern "C" int32_t pararnn_scan_diag(const float* A, const float* b, const float* s0, float* s, void* ws,
                                      size_t ws_bytes, const pararnn_opts* o, void* stream) {
   return scan(1, A, b, s0, s, ws, ws_bytes, o, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int32_t pararnn_scan_dense(const float* A, const float* b, const float* s0, float* s, void* ws,
+                                      size_t ws_bytes, const pararnn_opts* o, void* stream) {
+  return scan_dense(A, b, s0, s, ws, ws_bytes, o, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int32_t pararnn_scan_block2(const float* A, const float* b, const float* s0, float* s, void* ws,

@@ -1,0 +1,309 @@
+// scan_dense.h -- the linear recurrence with a dense n x n matrix per step,
+//   s_l = A_l s_{l-1} + b_l,   s_{-1} = s0,   n <= 32,
+// the linearised system of a generic RNN whose Jacobians are dense (ParaRNN
+// article, cafecomtech.com, section "Engenharia pra escalar": storage grows as
+// n^2 and the products as n^3, which is why the diagonal cells exist; for
+// small n it is still a few GEMM-shaped products per step).
+//
+// Four launches over chunks of kDenseChunk steps of one batch row:
+//   1. dense_chunk_kernel: the transfer P = A_end ... A_start (a chain of
+//      32 x 32 x 32 products on the matrix cores, fp32) and local solution v
+//      from zero of every segment of kDenseSeg steps (one wave each), and of
+//      the chunk, the segments combined by a tree through LDS;
+//   2. dense_carry_kernel: per batch row, the carries into the chunks,
+//      x_{c+1} = P_c x_c + v_c from s0, one matrix-vector product per chunk;
+//   3. dense_segcarry_kernel: per chunk, the carries into its segments;
+//   4. dense_apply_kernel: per segment, the recurrence itself from its carry,
+//      one matrix-vector product per step, writing s.
+// Everything runs in a 32 x 32 frame: entries past n are zero, and so stay
+// the padded state components.
+//
+// Matrix-core layout (v_mfma_f32_32x32x2f32, one 64-lane wave): lane
+// (j, h) = (lane % 32, lane / 32) holds accumulator slots r = 0..15 with the
+// entries D[R(r, h)][j], R(r, h) = 8 (r / 4) + 4 h + r % 4. Product step r
+// contracts over the index pair (R(r, 0), R(r, 1)): lane (i, h) supplies
+// A[i][R(r, h)] and lane (j, h) supplies the previous product's own slot r,
+// so a chain Q <- A Q needs no data movement between products.
+#pragma once
+
+#include "device_common.h"
+
+namespace pararnn {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kDenseMaxN = 32;          // largest state size
+constexpr int kDenseSeg = 16;           // steps per wave in the transfer chain
+constexpr int kDenseWaves = 8;          // waves (segments) per chunk
+constexpr int kDenseChunk = kDenseSeg * kDenseWaves;
+constexpr int kDenseRing = 4;           // steps of A in flight per wave in the transfer chain
+
+__device__ __forceinline__ int dense_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+struct DenseArgs {
+  const float* A;   // [B][L][n][n]
+  const float* b;   // [B][L][n]
+  const float* s0;  // [B][n] or nullptr
+  float* s;         // [B][L][n]
+  float* P;         // [B][nchunks][32][32] chunk transfers (workspace)
+  float* v;         // [B][nchunks][32] chunk local solutions (workspace)
+  float* carry;     // [B][nchunks][32] carries into the chunks (workspace)
+  float* Pseg;      // [B][nchunks][kDenseWaves][32][32] segment transfers (workspace)
+  float* vseg;      // [B][nchunks][kDenseWaves][32] segment local solutions (workspace)
+  float* cseg;      // [B][nchunks][kDenseWaves][32] carries into the segments (workspace)
+  int B, L, n, nchunks;
+};
+
+// Row i of A_l at the 16 columns R(r, h) (zero past n), and b_l[i]. N32: n is
+// 32 and A is 16-byte aligned, so the four runs of four columns are vector
+// loads; otherwise the address is clamped into the matrix and the value
+// selected, so no load sits behind a branch.
+template <bool N32>
+__device__ __forceinline__ void dense_load_row(const DenseArgs& p, long long step, int i, int h, float (&a)[16],
+                                               float& bi) {
+  if constexpr (N32) {
+    const float* row = p.A + (step * 32 + i) * 32;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 q = *reinterpret_cast<const f32x4*>(row + 8 * g + 4 * h);
+      a[4 * g] = q.x;
+      a[4 * g + 1] = q.y;
+      a[4 * g + 2] = q.z;
+      a[4 * g + 3] = q.w;
+    }
+    bi = p.b[step * 32 + i];
+  } else {
+    const int ic = min(i, p.n - 1);
+    const float* row = p.A + (step * p.n + ic) * p.n;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int c = dense_row(r, h);
+      const float t = row[min(c, p.n - 1)];
+      a[r] = (i < p.n && c < p.n) ? t : 0.0f;
+    }
+    const float t = p.b[step * p.n + ic];
+    bi = (i < p.n) ? t : 0.0f;
+  }
+}
+
+// y[i] = sum_q a[i][q] x[q] + bi in lanes i and i + 32, with x[q] read from
+// this wave's LDS vector xl (lane (i, h) reads its four runs of four)
+__device__ __forceinline__ float dense_matvec(const float (&a)[16], const float* xl, int h, float bi) {
+  float pg[4];  // four independent partial sums shorten the dependent chain
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const f32x4 xv = *reinterpret_cast<const f32x4*>(xl + 8 * g + 4 * h);
+    pg[g] = a[4 * g] * xv.x;
+    pg[g] = fmaf(a[4 * g + 1], xv.y, pg[g]);
+    pg[g] = fmaf(a[4 * g + 2], xv.z, pg[g]);
+    pg[g] = fmaf(a[4 * g + 3], xv.w, pg[g]);
+  }
+  const float part = (pg[0] + pg[1]) + (pg[2] + pg[3]);
+  return part + __shfl_xor(part, 32, 64) + bi;
+}
+
+// Q <- A Q with A given as row values a (this lane's row, columns R(r, h))
+__device__ __forceinline__ f32x16 dense_mfma_chain(const float (&a)[16], const f32x16& Q) {
+  f32x16 out = {};
+#pragma unroll
+  for (int r = 0; r < 16; ++r) out = __builtin_amdgcn_mfma_f32_32x32x2f32(a[r], Q[r], out, 0, 0, 0);
+  return out;
+}
+
+template <bool N32>
+__global__ void __launch_bounds__(64 * kDenseWaves) dense_chunk_kernel(const DenseArgs p) {
+  __shared__ float s_q[kDenseWaves / 2][32][33];  // transfers handed down the tree (padded rows)
+  __shared__ float s_v[kDenseWaves / 2][32];
+  __shared__ __align__(16) float s_x[kDenseWaves][32];  // each wave's running vector
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = lane & 31, h = lane >> 5;
+  const int b = blockIdx.x / p.nchunks, c = blockIdx.x - b * p.nchunks;
+  const int l_begin = c * kDenseChunk + wave * kDenseSeg;
+  const int l_end = min(l_begin + kDenseSeg, p.L);
+  const long long row0 = static_cast<long long>(b) * p.L;
+  float* xl = s_x[wave];
+
+  // segment transfer Q (accumulator layout) and local solution v (lane i, both halves)
+  f32x16 Q;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) Q[r] = (dense_row(r, h) == j) ? 1.0f : 0.0f;
+  float v = 0.0f;
+  if (h == 0) xl[j] = 0.0f;
+  // rows stream through a ring of kDenseRing steps ahead of the chain
+  float a[kDenseRing][16], bs[kDenseRing];
+#pragma unroll
+  for (int t = 0; t < kDenseRing; ++t) {
+    if (l_begin + t < l_end) dense_load_row<N32>(p, row0 + l_begin + t, j, h, a[t], bs[t]);
+  }
+#pragma unroll
+  for (int t = 0; t < kDenseSeg; ++t) {
+    if (l_begin + t < l_end) {
+      const int k = t % kDenseRing;
+      v = dense_matvec(a[k], xl, h, bs[k]);
+      if (h == 0) xl[j] = v;
+      Q = dense_mfma_chain(a[k], Q);
+      if (t + kDenseRing < kDenseSeg && l_begin + t + kDenseRing < l_end)
+        dense_load_row<N32>(p, row0 + l_begin + t + kDenseRing, j, h, a[k], bs[k]);
+    }
+  }
+
+  {  // the segment's own transfer, for the carries into the segments
+    const long long sg = (static_cast<long long>(b) * p.nchunks + c) * kDenseWaves + wave;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p.Pseg[sg * 1024 + dense_row(r, h) * 32 + j] = Q[r];
+    if (h == 0) p.vseg[sg * 32 + j] = v;
+  }
+
+  // tree over the waves: at distance d, wave w (w % 2d == 0) takes the
+  // segment of wave w + d, which follows it: Q_w <- Q_{w+d} Q_w, v_w <- Q_{w+d} v_w + v_{w+d}
+  for (int d = 1; d < kDenseWaves; d *= 2) {
+    const bool giver = (wave % (2 * d)) == d;
+    const int slot = wave / (2 * d);
+    if (giver) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_q[slot][dense_row(r, h)][j] = Q[r];
+      if (h == 0) s_v[slot][j] = v;
+    }
+    __syncthreads();
+    if ((wave % (2 * d)) == 0) {
+      float aq[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) aq[r] = s_q[slot][j][dense_row(r, h)];
+      v = dense_matvec(aq, xl, h, s_v[slot][j]);
+      if (h == 0) xl[j] = v;
+      Q = dense_mfma_chain(aq, Q);
+    }
+    __syncthreads();
+  }
+  if (wave == 0) {
+    float* P = p.P + (static_cast<long long>(b) * p.nchunks + c) * 1024;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) P[dense_row(r, h) * 32 + j] = Q[r];
+    if (h == 0) p.v[(static_cast<long long>(b) * p.nchunks + c) * 32 + j] = v;
+  }
+}
+
+// One wave per batch row: carries into every chunk, in order. The chunk
+// transfers stream kDenseCarryAhead chunks ahead of the chain.
+constexpr int kDenseCarryAhead = 4;
+__global__ void __launch_bounds__(64) dense_carry_kernel(const DenseArgs p) {
+  __shared__ __align__(16) float xl[32];
+  const int lane = threadIdx.x, j = lane & 31, h = lane >> 5;
+  const int b = blockIdx.x;
+  const long long base = static_cast<long long>(b) * p.nchunks;
+  float x = (p.s0 && j < p.n) ? p.s0[static_cast<long long>(b) * p.n + min(j, p.n - 1)] : 0.0f;
+  if (h == 0) xl[j] = x;
+  float ring[kDenseCarryAhead][16], vring[kDenseCarryAhead];
+  auto load = [&](int c, float (&aa)[16], float& vv) {
+    const float* P = p.P + (base + c) * 1024 + j * 32;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 q = *reinterpret_cast<const f32x4*>(P + 8 * g + 4 * h);
+      aa[4 * g] = q.x;
+      aa[4 * g + 1] = q.y;
+      aa[4 * g + 2] = q.z;
+      aa[4 * g + 3] = q.w;
+    }
+    vv = p.v[(base + c) * 32 + j];
+  };
+#pragma unroll
+  for (int k = 0; k < kDenseCarryAhead; ++k)
+    if (k < p.nchunks) load(k, ring[k], vring[k]);
+  for (int c0 = 0; c0 < p.nchunks; c0 += kDenseCarryAhead) {
+#pragma unroll
+    for (int k = 0; k < kDenseCarryAhead; ++k) {
+      const int c = c0 + k;
+      if (c < p.nchunks) {
+        if (h == 0) p.carry[(base + c) * 32 + j] = x;
+        x = dense_matvec(ring[k], xl, h, vring[k]);
+        if (h == 0) xl[j] = x;
+        if (c + kDenseCarryAhead < p.nchunks) load(c + kDenseCarryAhead, ring[k], vring[k]);
+      }
+    }
+  }
+}
+
+// one wave per chunk: the carries into its segments, from the chunk's carry
+// and the segment transfers in order
+__global__ void __launch_bounds__(64) dense_segcarry_kernel(const DenseArgs p) {
+  __shared__ __align__(16) float xl[32];
+  const int lane = threadIdx.x, j = lane & 31, h = lane >> 5;
+  const long long cb = blockIdx.x;  // b * nchunks + c
+  float x = p.carry[cb * 32 + j];
+  if (h == 0) xl[j] = x;
+  float a[16], vi;
+  auto load = [&](int w, float (&aa)[16], float& vv) {
+    const float* P = p.Pseg + (cb * kDenseWaves + w) * 1024 + j * 32;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 q = *reinterpret_cast<const f32x4*>(P + 8 * g + 4 * h);
+      aa[4 * g] = q.x;
+      aa[4 * g + 1] = q.y;
+      aa[4 * g + 2] = q.z;
+      aa[4 * g + 3] = q.w;
+    }
+    vv = p.vseg[(cb * kDenseWaves + w) * 32 + j];
+  };
+  load(0, a, vi);
+#pragma unroll
+  for (int w = 0; w < kDenseWaves; ++w) {
+    float an[16], vn = 0.0f;
+    if (w + 1 < kDenseWaves - 1) load(w + 1, an, vn);
+    if (h == 0) p.cseg[(cb * kDenseWaves + w) * 32 + j] = x;
+    if (w + 1 < kDenseWaves) {
+      x = dense_matvec(a, xl, h, vi);
+      if (h == 0) xl[j] = x;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) a[r] = an[r];
+      vi = vn;
+    }
+  }
+}
+
+// one wave per segment: the recurrence from the segment's carry; the rows of
+// A stream in groups of kDenseGroup steps, the next group in flight while the
+// current one is applied
+constexpr int kDenseGroup = 4;
+template <bool N32>
+__global__ void __launch_bounds__(64) dense_apply_kernel(const DenseArgs p) {
+  __shared__ __align__(16) float xl[32];
+  const int lane = threadIdx.x, j = lane & 31, h = lane >> 5;
+  const long long sg = blockIdx.x;  // (b * nchunks + c) * kDenseWaves + w
+  const int b = static_cast<int>(sg / (static_cast<long long>(p.nchunks) * kDenseWaves));
+  const int cw = static_cast<int>(sg - static_cast<long long>(b) * p.nchunks * kDenseWaves);  // c * W + w
+  const long long row0 = static_cast<long long>(b) * p.L;
+  const int l_begin = cw * kDenseSeg, l_end = min(l_begin + kDenseSeg, p.L);
+  if (l_begin >= p.L) return;  // segment past the end of the sequence (uniform per wave)
+  float x = p.cseg[sg * 32 + j];
+  if (h == 0) xl[j] = x;
+  float a[2][kDenseGroup][16], bs[2][kDenseGroup];
+  auto load_group = [&](int g0, float (&ag)[kDenseGroup][16], float (&bg)[kDenseGroup]) {
+#pragma unroll
+    for (int t = 0; t < kDenseGroup; ++t) {
+      if (g0 + t < l_end) dense_load_row<N32>(p, row0 + g0 + t, j, h, ag[t], bg[t]);
+    }
+  };
+  load_group(l_begin, a[0], bs[0]);
+  for (int g0 = l_begin; g0 < l_end; g0 += 2 * kDenseGroup) {
+    if (g0 + kDenseGroup < l_end) load_group(g0 + kDenseGroup, a[1], bs[1]);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int gs = g0 + half * kDenseGroup;
+      // the group after next starts loading while the second one is applied
+      if (half == 1 && g0 + 2 * kDenseGroup < l_end) load_group(g0 + 2 * kDenseGroup, a[0], bs[0]);
+#pragma unroll
+      for (int t = 0; t < kDenseGroup; ++t) {
+        const int l = gs + t;
+        if (l < l_end) {
+          x = dense_matvec(a[half][t], xl, h, bs[half][t]);
+          if (h == 0) {
+            xl[j] = x;
+            if (j < p.n) p.s[(row0 + l) * p.n + j] = x;
+          }
+        }
+      }
+    }
+  }
+}
+
+}  // namespace pararnn

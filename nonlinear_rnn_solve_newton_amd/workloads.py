@@ -187,3 +187,53 @@ def make_scan_inputs(ns: int, B: int, L: int, D: int, *, seed: int, amax: float 
 
 def scan_workload_inputs(w: ScanWorkload) -> ScanInputs:
     return make_scan_inputs(w.ns, w.B, w.L, w.D, seed=w.seed, amax=w.amax)
+
+
+# ---------------------------------------------------------------------------
+# Dense recurrence (n x n matrix per step): A_l = 0.95 Q_l with Q_l a random
+# orthogonal matrix (QR of a Gaussian matrix, signs fixed by diag(R) > 0), so
+# every step contracts by exactly 0.95 in the 2-norm; then b ~ N(0, 1),
+# s0 ~ N(0, 1), drawn in that order.
+
+@dataclass(frozen=True)
+class DenseScanWorkload:
+    name: str
+    B: int
+    L: int
+    n: int
+    seed: int
+    scale: float = 0.95
+
+    @property
+    def N(self) -> int:
+        return self.B * self.L * self.n
+
+
+DENSE_WORKLOADS = {
+    w.name: w
+    for w in [
+        DenseScanWorkload("scan_dense_b8_l4096_n32", 8, 4096, 32, seed=7),
+    ]
+}
+
+
+@dataclass
+class DenseScanInputs:
+    A: torch.Tensor   # [B][L][n][n] fp32, CPU
+    b: torch.Tensor   # [B][L][n]
+    s0: torch.Tensor  # [B][n]
+
+
+def make_dense_scan_inputs(B: int, L: int, n: int, *, seed: int, scale: float = 0.95) -> DenseScanInputs:
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    M = torch.randn(B, L, n, n, generator=g, dtype=torch.float64)
+    Q, R = torch.linalg.qr(M)
+    Q = Q * torch.sign(torch.diagonal(R, dim1=-2, dim2=-1)).unsqueeze(-2)
+    A = (scale * Q).to(torch.float32)
+    b = torch.randn(B, L, n, generator=g, dtype=torch.float32)
+    s0 = torch.randn(B, n, generator=g, dtype=torch.float32)
+    return DenseScanInputs(A=A.contiguous(), b=b.contiguous(), s0=s0.contiguous())
+
+
+def dense_workload_inputs(w: DenseScanWorkload) -> DenseScanInputs:
+    return make_dense_scan_inputs(w.B, w.L, w.n, seed=w.seed, scale=w.scale)

@@ -20,7 +20,8 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = b.header_functions()
     assert set(names) == {"pararnn_workspace_bytes", "pararnn_solve_gru", "pararnn_solve_lstm",
-                          "pararnn_adjoint", "pararnn_scan_diag", "pararnn_scan_block2", "pararnn_strerror"}
+                          "pararnn_adjoint", "pararnn_scan_diag", "pararnn_scan_block2", "pararnn_scan_dense",
+                          "pararnn_strerror"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -142,3 +143,19 @@ def test_scan_invalid_arguments_rejected_before_launch(lib, fn):
     assert st(ws_bytes=0) == -3
     assert st(ws_off=16) == -2
     assert f(P(1), P(1), None, P(1), P(2), 1 << 40, None, None) == -1
+
+
+def test_scan_dense_workspace_and_invalid_arguments(lib):
+    o, _ = b.make_opts(8, 4096, 32, 0)
+    n = lib.pararnn_workspace_bytes(b.GRU, b.OP_SCAN_DENSE, ctypes.byref(o))
+    assert n >= 8 * 32 * (1024 + 64) * 4  # transfers, local solutions and carries per 128-step chunk
+    o33, _ = b.make_opts(1, 10, 33, 0)
+    assert lib.pararnn_workspace_bytes(b.GRU, b.OP_SCAN_DENSE, ctypes.byref(o33)) == 0  # n <= 32
+    P = lambda v: ctypes.c_void_p(v * 4096) if v else None  # noqa: E731  (never dereferenced)
+    f = lib.pararnn_scan_dense
+    assert f(P(0), P(1), None, P(1), P(2), 1 << 40, ctypes.byref(o), None) == -1
+    assert f(P(1), P(1), None, P(0), P(2), 1 << 40, ctypes.byref(o), None) == -1
+    assert f(P(1), P(1), None, P(1), P(2), 1 << 40, ctypes.byref(o33), None) == -1
+    assert f(P(1), P(1), None, P(1), P(2), 16, ctypes.byref(o), None) == -3
+    assert f(P(1), P(1), None, P(1), ctypes.c_void_p(2 * 4096 + 16), 1 << 40, ctypes.byref(o), None) == -2
+    assert f(ctypes.c_void_p(4097), P(1), None, P(1), P(2), 1 << 40, ctypes.byref(o), None) == -2  # misaligned A
