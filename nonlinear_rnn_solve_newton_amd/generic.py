@@ -40,21 +40,41 @@ def newton_solve(step: Callable, x, s0: Optional[torch.Tensor] = None, *, B: int
     block = 2: the state is a pair of components, stacked [2][B][L][D];
                step(P, x) -> f with P and f of that shape (2x2 Jacobian blocks
                per channel).
+    block = "dense": the state is [B][L][D] with D <= 32 and a dense D x D
+               Jacobian per step (a generic RNN, ParaRNN article section
+               "Engenharia pra escalar": n^2 storage, n^3 products); its D
+               columns come from D tangents, and the linear system is solved by
+               pararnn_scan_dense.
     x is passed to step unchanged (e.g. precomputed gate inputs [B][L][G][D]).
     s0: [B][D] (block 1) or [2][B][D] (block 2) fp32, or None for zero.
     Returns the K-th iterate (and the per-iteration max |update| if asked).
     """
-    if block not in (1, 2):
-        raise ValueError("block must be 1 or 2")
+    if block not in (1, 2, "dense"):
+        raise ValueError("block must be 1, 2 or 'dense'")
     dev = x.device if isinstance(x, torch.Tensor) else torch.device("cuda:0")
-    shape = (B, L, D) if block == 1 else (2, B, L, D)
-    l_axis = 1 if block == 1 else 2
+    shape = (2, B, L, D) if block == 2 else (B, L, D)
+    l_axis = 2 if block == 2 else 1
     S = torch.zeros(shape, dtype=torch.float32, device=dev)
     ws = None
     updates = []
     fn = lambda p: step(p, x)  # noqa: E731
     for _ in range(iters):
         P = _shift(S, s0, l_axis)
+        if block == "dense":
+            cols = []
+            for k in range(D):  # column k of every step's Jacobian
+                e = torch.zeros_like(P)
+                e[..., k] = 1.0
+                f, ck = torch.func.jvp(fn, (P,), (e,))
+                cols.append(ck)
+            A = torch.stack(cols, dim=-1)  # [B][L][D][D], A[..., r, k] = df_r / ds_k
+            b = f - (A @ P.unsqueeze(-1)).squeeze(-1)
+            r = binding.scan_dense(A.contiguous().float(), b.contiguous().float(), s0, ws=ws)
+            ws = r["ws"]
+            if return_updates:
+                updates.append(float((r["s"] - S).abs().max()))
+            S = r["s"]
+            continue
         if block == 1:
             f, A = torch.func.jvp(fn, (P,), (torch.ones_like(P),))
             b = f - A * P

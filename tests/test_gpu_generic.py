@@ -70,3 +70,60 @@ def test_generic_tier_on_a_cell_without_a_kernel():
     S, upd = generic.newton_solve(step, ud, s0d, B=B, L=L, D=D, iters=12, return_updates=True)
     assert upd[-1] < 1e-5 and upd[-1] < upd[2]
     assert_close(S.cpu().double().numpy(), want, STATE_TOL, "fixed point vs sequential")
+
+
+def _elman_dense_newton_numpy(u, W, s0, K):
+    """Newton on F_l(S) = S_l - tanh(W S_{l-1} + u_l) for one row, each step a
+    dense (L n) x (L n) solve (numpy.linalg.solve), from S = 0."""
+    L, n = u.shape
+    S = np.zeros((L, n))
+    for _ in range(K):
+        P = np.vstack([s0[None], S[:-1]])
+        f = np.tanh(P @ W.T + u)
+        F = (S - f).reshape(-1)
+        J = np.eye(L * n)
+        for l in range(1, L):
+            J[l * n:(l + 1) * n, (l - 1) * n:l * n] = -(1 - f[l] ** 2)[:, None] * W
+        S = S - np.linalg.solve(J, F).reshape(L, n)
+    return S
+
+
+@pytest.mark.parametrize("n", [4, 32])
+def test_generic_dense_elman_matches_dense_newton(n):
+    """A dense-Jacobian RNN (h' = tanh(W h + u), W dense) through the generic
+    tier and pararnn_scan_dense: each Newton iterate equals the same iteration
+    with the whole system solved densely."""
+    say(f"generic dense Elman n={n}")
+    B, L = 2, 40
+    g = torch.Generator().manual_seed(90 + n)
+    W = 0.9 * torch.linalg.qr(torch.randn(n, n, generator=g, dtype=torch.float64))[0]
+    u = torch.randn(B, L, n, generator=g)
+    s0 = torch.randn(B, n, generator=g)
+    dev = torch.device("cuda:0")
+    Wd = W.float().to(dev)
+    step = lambda h, uu: torch.tanh(h @ Wd.T + uu)  # noqa: E731
+    for K in (1, 3):
+        S = generic.newton_solve(step, u.to(dev), s0.to(dev), B=B, L=L, D=n, iters=K, block="dense")
+        got = S.cpu().double().numpy()
+        want = np.stack([_elman_dense_newton_numpy(u[b].double().numpy(), W.numpy(), s0[b].double().numpy(), K)
+                         for b in range(B)])
+        assert_close(got, want, STATE_TOL, f"dense Elman K={K}")
+
+
+def test_generic_dense_elman_fixed_point():
+    """Iterated to convergence the dense tier reproduces the sequential recurrence."""
+    B, L, n = 3, 500, 16
+    g = torch.Generator().manual_seed(93)
+    W = 0.8 * torch.linalg.qr(torch.randn(n, n, generator=g, dtype=torch.float64))[0]
+    u = torch.randn(B, L, n, generator=g)
+    want = torch.empty(B, L, n, dtype=torch.float64)
+    h = torch.zeros(B, n, dtype=torch.float64)
+    for l in range(L):
+        h = torch.tanh(h @ W.T + u[:, l].double())
+        want[:, l] = h
+    dev = torch.device("cuda:0")
+    Wd = W.float().to(dev)
+    S, upd = generic.newton_solve(lambda hh, uu: torch.tanh(hh @ Wd.T + uu), u.to(dev), B=B, L=L, D=n, iters=12,
+                                  block="dense", return_updates=True)
+    assert upd[-1] < 1e-5
+    assert_close(S.cpu().double().numpy(), want.numpy(), STATE_TOL, "dense fixed point vs sequential")
