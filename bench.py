@@ -124,12 +124,16 @@ def traffic_from_counters(workload: str, fetch_csv: str, write_csv: str, iters: 
         rows.sort(key=lambda r: int(r["Dispatch_Id"]))
         copy = [float(r["Counter_Value"]) * 1024 for r in rows
                 if "copyBuffer" in r["Kernel_Name"] and float(r["Counter_Value"]) > 1e5]
-        its = [float(r["Counter_Value"]) * 1024 for r in rows if f"{kernel}_kernel" in r["Kernel_Name"]]
+        tag = "pararnn::dense_" if kernel == "dense" else f"{kernel}_kernel"
+        its = [float(r["Counter_Value"]) * 1024 for r in rows if tag in r["Kernel_Name"]]
         return copy, its
 
     calib = float(1 << 30)
     fc, fi = read(fetch_csv, "FETCH_SIZE")
     wc, wi = read(write_csv, "WRITE_SIZE")
+    if kernel == "dense":  # four launches per scan: sum each scan's launches
+        fi = [sum(fi[i:i + 4]) for i in range(0, len(fi) - 3, 4)]
+        wi = [sum(wi[i:i + 4]) for i in range(0, len(wi) - 3, 4)]
     fscale = calib / (sum(fc) / len(fc))
     wscale = calib / (sum(wc) / len(wc))
     # dispatches come in solves of `iters` launches; average each launch index
@@ -271,11 +275,19 @@ def bench_scan_dense(w, args):
         "config": {"workload": w.name, "B": w.B, "L": w.L, "n": w.n},
         "roofline": {"bound": "hbm", "kernel": "dense_chunk_kernel + dense_carry_kernel + dense_segcarry_kernel + dense_apply_kernel",
                      "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-                     "traffic": None, "algorithmic_bytes_per_launch": [nbytes], "launch_ms": [t]},
+                     "traffic": load_traffic(w.name, source_digest(), "dense"),
+                     "algorithmic_bytes_per_launch": [nbytes], "launch_ms": [t]},
         "matrix_cores": {"achieved": flops / (t * 1e-3) / 1e12, "peak": PEAK_F32_MATRIX_TFLOPS,
                          "unit": "TFLOP/s", "frac": flops / (t * 1e-3) / 1e12 / PEAK_F32_MATRIX_TFLOPS},
         "timing": {"scan_ms": t, "source_digest": source_digest()},
     }
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = src.numel() * 4
     if not args.no_cpu_baseline:
         from oracle import oracle as O
         nthreads = O.default_threads()
@@ -426,6 +438,9 @@ def main(argv=None):
         if name in SCAN_WORKLOADS:
             d = traffic_from_counters(name, *args.traffic_from, iters=1, kernel="scan")
             traffic_path(name, "scan").write_text(json.dumps(d, indent=1) + "\n")
+        elif name in DENSE_WORKLOADS:
+            d = traffic_from_counters(name, *args.traffic_from, iters=1, kernel="dense")
+            traffic_path(name, "dense").write_text(json.dumps(d, indent=1) + "\n")
         else:
             d = traffic_from_counters(name, *args.traffic_from, iters=WORKLOADS[name].iters)
             traffic_path(name).write_text(json.dumps(d, indent=1) + "\n")
