@@ -20,6 +20,22 @@
 // take tickets in chunk-major order and only ever wait for earlier tickets,
 // so no residency of the whole grid is needed.
 //
+// Latency hiding inside an iteration:
+//   - every wave reads the predecessor chunk's inclusive carry halfway through
+//     its cell evaluations, so in the common case (the predecessor has already
+//     published it) the carry is in registers when the local scan ends, and
+//     the look-back round trip to memory is off the critical path; only when
+//     that early read finds nothing does the wave publish the chunk aggregate
+//     and walk back through the descriptors;
+//   - each wave forms its own carry-in from the chunk carry and the preceding
+//     waves' aggregates, so one barrier per iteration is enough; the last wave
+//     publishes the chunk's inclusive carry;
+//   - the iterate at the row before a lane group's first step, its next
+//     linearisation point, is kept as a running sum: it moves by the carry
+//     entering the lane group (the update d at that row), with no exchange;
+//   - per-wave maxima of |d| leave through a cross-lane (DPP) reduction, one
+//     word per wave, reduced over the grid by the finalize launch.
+//
 // UKEEP: keep the gate inputs in registers for all iterations (one HBM read
 // per solve) or stream them again in every iteration (fewer registers).
 #pragma once
@@ -36,20 +52,31 @@ struct FusedArgs {
   unsigned long long* incl;  // [K][nchunks][NS][slots]
   unsigned long long* agg;   // [K][nchunks][NS*NS+NS][slots]
   unsigned int* ctr;         // [0] ticket
-  unsigned int* pmax;        // [K][B][nchunks][ntiles_d] per-workgroup max |update| bits
+  unsigned int* pmax;        // [K][B][nchunks][ntiles_d][W] per-wave max |update| bits
   int B, L, D, K, nchunks, ntiles_d;
 };
+
+// Maximum over the wave of a value whose bit pattern orders like an unsigned
+// integer (non-negative floats, NaN above +inf), returned to every lane: row
+// reductions by quad and row rotations, then row broadcasts into lane 63.
+__device__ __forceinline__ uint32_t wave_max_bits(uint32_t v) {
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xb1, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4e, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x124, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x128, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x142, 0xa, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x143, 0xc, 0xf, false)));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
 
 template <class Cell, class UT, int C, int T, int W, int LL, int OCC, bool UKEEP>
 __global__ void __launch_bounds__(64 * W, OCC) newton_fused_kernel(const FusedArgs p) {
   constexpr int NS = Cell::NS, G = Cell::G;
-  constexpr int LD = 64 / LL, CW = LD * C, CL = W * LL * T, NA = NS * NS + NS, NSEG = W * LL;
+  constexpr int LD = 64 / LL, CW = LD * C, CL = W * LL * T, NA = NS * NS + NS;
+  constexpr int TPOLL = T / 2;  // the predecessor's carry is read before this step
 
-  __shared__ float s_agg[W][NA][CW];
-  __shared__ float s_carry[NS][CW];
-  __shared__ float s_last[NSEG][NS][CW];
+  __shared__ float s_agg[2][W][NA][CW];  // per-wave aggregates, double-buffered over iterations
   __shared__ unsigned int s_ticket;
-  __shared__ uint32_t s_wmax[W];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -85,6 +112,10 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_fused_kernel(const FusedAr
 #pragma unroll
   for (int s = 0; s < NS; ++s) rout[s] = make_rsrc(p.sout[s] + wrow * p.D, rows * sstep);
   const int dc = dv ? d0 : p.D - C;  // channel group for the per-channel loads
+  const bool pred = chunk > 0;       // the chunk carry comes from predecessor chunks
+  // per-wave maxima: [K][B][nchunks][ntiles_d][W]
+  unsigned int* pmax = p.pmax + ((static_cast<long long>(b) * p.nchunks + chunk) * p.ntiles_d + dt0 / CW) * W + wave;
+  const long long pmax_k = static_cast<long long>(p.B) * p.nchunks * p.ntiles_d * W;
 
   auto tile_body = [&](auto full_tag) {
   constexpr bool FULL = decltype(full_tag)::value;
@@ -98,7 +129,8 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_fused_kernel(const FusedAr
 #pragma unroll
       for (int g = 0; g < G; ++g) uu[t][g].load(ru, vu0 + t * ustep, static_cast<uint32_t>(g) * gstep);
   }
-  // iterate k-1 at the lane's steps (S^(0) = 0) and at the chunk boundary
+  // iterate k-1 at the lane's steps (S^(0) = 0), and at the row before the
+  // lane group's first step (the fixed initial state before the sequence)
   float so[T][NS][C];
 #pragma unroll
   for (int t = 0; t < T; ++t)
@@ -106,12 +138,12 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_fused_kernel(const FusedAr
     for (int s = 0; s < NS; ++s)
 #pragma unroll
       for (int c = 0; c < C; ++c) so[t][s][c] = 0.0f;
-  float sb[NS][C];
+  float sp[NS][C];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
 #pragma unroll
-    for (int c = 0; c < C; ++c) sb[s][c] = 0.0f;
-    if (chunk == 0 && p.s0[s]) ld_f32<C>(p.s0[s] + static_cast<long long>(b) * p.D + dc, sb[s]);
+    for (int c = 0; c < C; ++c) sp[s][c] = 0.0f;
+    if (chunk == 0 && q == 0 && p.s0[s]) ld_f32<C>(p.s0[s] + static_cast<long long>(b) * p.D + dc, sp[s]);
   }
 
   // one Newton iteration; ZERO: the first, evaluated at the zero iterate
@@ -119,16 +151,30 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_fused_kernel(const FusedAr
   auto iterate = [&](int k, auto zero_tag) {
     constexpr bool ZERO = decltype(zero_tag)::value;
     const uint32_t tag = static_cast<uint32_t>(k);
-    float sp[NS][C];  // iterate k-1 at the row before the lane's first step
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-      for (int c = 0; c < C; ++c) sp[s][c] = (q == 0) ? sb[s][c] : (ZERO ? 0.0f : s_last[q - 1][s][ld * C + c]);
+    const int buf = k & 1;
+    unsigned long long* incl = p.incl + (k - 1) * inc_k;
+    unsigned long long* agg = p.agg + (k - 1) * agg_k;
+    unsigned long long early[NS][C];  // the predecessor's inclusive carry, read early
     float Jt[T][NS][NS][C], rt[T][NS][C];
     Aff<NS, C> acc;
     acc.set_identity();
 #pragma unroll
     for (int t = 0; t < T; ++t) {
+      if (t == TPOLL) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+          for (int c = 0; c < C; ++c) early[s][c] = 0ull;
+        if (pred) {
+#pragma unroll
+          for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+              early[s][c] = desc_get(incl + (static_cast<long long>(chunk - 1) * NS + s) * BD + chan + c * LD);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
       URaw<UT, C> ut[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
@@ -171,83 +217,75 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_fused_kernel(const FusedAr
 #pragma unroll
         for (int c = 0; c < C; ++c) {
 #pragma unroll
-          for (int s = 0; s < NS; ++s) s_agg[wave][r * NS + s][ld * C + c] = acc.A[r][s][c];
-          s_agg[wave][NS * NS + r][ld * C + c] = acc.b[r][c];
+          for (int s = 0; s < NS; ++s) s_agg[buf][wave][r * NS + s][ld * C + c] = acc.A[r][s][c];
+          s_agg[buf][wave][NS * NS + r][ld * C + c] = acc.b[r][c];
         }
     }
     __syncthreads();
 
-    if (wave == 0 && ll == 0) {
-      float carry[NS][C];
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int c = 0; c < C; ++c) carry[s][c] = 0.0f;
-      if (dv && p.nchunks > 1) {
-        Aff<NS, C> tot;
-        tot.set_identity();
-#pragma unroll
-        for (int w = 0; w < W; ++w) {
-          Aff<NS, C> e;
-#pragma unroll
-          for (int r = 0; r < NS; ++r)
-#pragma unroll
-            for (int c = 0; c < C; ++c) {
-#pragma unroll
-              for (int s = 0; s < NS; ++s) e.A[r][s][c] = s_agg[w][r * NS + s][ld * C + c];
-              e.b[r][c] = s_agg[w][NS * NS + r][ld * C + c];
-            }
-          e.after(tot);
-          tot = e;
-        }
-        unsigned long long* incl = p.incl + (k - 1) * inc_k;
-        unsigned long long* agg = p.agg + (k - 1) * agg_k;
-        if (chunk > 0) {
-          if (chunk < p.nchunks - 1) publish_agg<NS, C>(agg, BD, chan, LD, chunk, tag, tot);
-          lookback<NS, C>(incl, agg, BD, chan, LD, chunk, -1, p.nchunks, tag, carry);
-        }
-        if (chunk < p.nchunks - 1) {
-          float x[NS][C];
-#pragma unroll
-          for (int s = 0; s < NS; ++s)
-#pragma unroll
-            for (int c = 0; c < C; ++c) x[s][c] = carry[s][c];
-          tot.apply(x);
-          publish_incl<NS, C>(incl, BD, chan, LD, chunk, tag, x);
-        }
-      }
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int c = 0; c < C; ++c) s_carry[s][ld * C + c] = carry[s][c];
-    }
-    __syncthreads();
-
-    float x[NS][C];
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-      for (int c = 0; c < C; ++c) x[s][c] = s_carry[s][ld * C + c];
-    // the chunk boundary moves by the carry entering the chunk
-    if (q == 0) {
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int c = 0; c < C; ++c) sb[s][c] += x[s][c];
-    }
-    for (int w = 0; w < wave; ++w) {
+    auto wave_agg = [&](int w) {
       Aff<NS, C> e;
 #pragma unroll
       for (int r = 0; r < NS; ++r)
 #pragma unroll
         for (int c = 0; c < C; ++c) {
 #pragma unroll
-          for (int s = 0; s < NS; ++s) e.A[r][s][c] = s_agg[w][r * NS + s][ld * C + c];
-          e.b[r][c] = s_agg[w][NS * NS + r][ld * C + c];
+          for (int s = 0; s < NS; ++s) e.A[r][s][c] = s_agg[buf][w][r * NS + s][ld * C + c];
+          e.b[r][c] = s_agg[buf][w][NS * NS + r][ld * C + c];
         }
-      e.apply(x);
+      return e;
+    };
+
+    // the chunk carry: the update d^(k) at the row before the chunk
+    float x[NS][C];
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int c = 0; c < C; ++c) x[s][c] = 0.0f;
+    if (pred && dv) {
+      bool ok = true;
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int c = 0; c < C; ++c) ok = ok && desc_ok(early[s][c], tag);
+      if (ok) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+          for (int c = 0; c < C; ++c) x[s][c] = desc_val(early[s][c]);
+      } else {
+        if (wave == W - 1 && ll == 0 && chunk < p.nchunks - 1) {
+          Aff<NS, C> tot = wave_agg(0);
+#pragma unroll
+          for (int w = 1; w < W; ++w) {
+            Aff<NS, C> e = wave_agg(w);
+            e.after(tot);
+            tot = e;
+          }
+          publish_agg<NS, C>(agg, BD, chan, LD, chunk, tag, tot);
+        }
+        lookback<NS, C>(incl, agg, BD, chan, LD, chunk, -1, p.nchunks, tag, x);
+      }
+    }
+    // through the preceding waves of the chunk
+#pragma unroll
+    for (int w = 0; w < W - 1; ++w)
+      if (w < wave) wave_agg(w).apply(x);
+    if (wave == W - 1 && ll == 0 && dv && chunk < p.nchunks - 1) {
+      float xi[NS][C];
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int c = 0; c < C; ++c) xi[s][c] = x[s][c];
+      wave_agg(W - 1).apply(xi);
+      publish_incl<NS, C>(incl, BD, chan, LD, chunk, tag, xi);
     }
     if constexpr (LL > 1) excl.apply(x);
+    // the next linearisation point at the row before the lane group
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int c = 0; c < C; ++c) sp[s][c] += x[s][c];
 
     float mx = 0.0f;
 #pragma unroll
@@ -272,20 +310,8 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_fused_kernel(const FusedAr
           if (valid) mx = __builtin_elementwise_maximum(mx, fabsf(y[r][c]));
         }
     }
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-      for (int c = 0; c < C; ++c) s_last[q][s][ld * C + c] = so[T - 1][s][c];
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, off, 64));
-    if (lane == 0) s_wmax[wave] = __float_as_uint(mx);
-    __syncthreads();
-    if (tid == 0) {
-      uint32_t m = s_wmax[0];
-#pragma unroll
-      for (int w = 1; w < W; ++w) m = max(m, s_wmax[w]);
-      p.pmax[((static_cast<long long>(k - 1) * p.B + b) * p.nchunks + chunk) * p.ntiles_d + dt0 / CW] = m;
-    }
+    const uint32_t m = wave_max_bits(__float_as_uint(mx));
+    if (lane == 0) pmax[(k - 1) * pmax_k] = m;
   };
 
   iterate(1, std::true_type{});

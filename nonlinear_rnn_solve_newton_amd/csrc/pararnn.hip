@@ -69,6 +69,7 @@ int scan_ns(int op) { return op == PARARNN_OP_SCAN_BLOCK2 ? 2 : 1; }
 // and channels
 struct Geo {
   int chunk, cw;
+  int pm = 1;  // partial row maxima per workgroup
 };
 
 template <int NS, int C>
@@ -106,7 +107,7 @@ Geo geo_for_c(int C) {
 template <class Cell, int C>
 constexpr Geo fused_geo() {
   using K = FusedCfg<Cell, C>;
-  return Geo{K::T * K::W * K::LL, (64 / K::LL) * C};
+  return Geo{K::T * K::W * K::LL, (64 / K::LL) * C, K::W};
 }
 
 template <class Cell>
@@ -188,7 +189,7 @@ Layout layout(int cell, int op, const pararnn_opts* o, bool with_da, Geo g, bool
   y.maxupd = off;
   off = round_up(off + sizeof(uint32_t) * static_cast<size_t>(K) * B);
   y.pmax = off;
-  if (op == PARARNN_OP_SOLVE) off = round_up(off + sizeof(uint32_t) * static_cast<size_t>(K) * nwg);
+  if (op == PARARNN_OP_SOLVE) off = round_up(off + sizeof(uint32_t) * static_cast<size_t>(K) * nwg * g.pm);
   y.incl = off;
   const size_t slots = B * static_cast<size_t>(y.ntiles_d) * g.cw;  // descriptor slots per component
   const size_t nk = fused ? static_cast<size_t>(K) : 1;  // descriptor sets
@@ -426,7 +427,7 @@ int solve(int cell, const void* u, const float* a, const float* c0, const float*
     }
     hipLaunchKernelGGL(newton_finalize_kernel, dim3(o->B, K), dim3(kRowmaxThreads), 0, stream,
                        static_cast<const unsigned int*>(fa.pmax), reinterpret_cast<unsigned int*>(w + y.maxupd),
-                       o->B, y.ntiles_d, y.nchunks, K, o->tol, 0, iters, converged, max_update);
+                       o->B, y.ntiles_d * g.pm, y.nchunks, K, o->tol, 0, iters, converged, max_update);
     return check_hip(hipGetLastError());
   }
   const size_t BLD = static_cast<size_t>(o->B) * o->L * o->D;
