@@ -29,7 +29,12 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak
 # vector ALU issue peak without packed fp32: 256 CUs x 64 lanes x 2.4 GHz
 # lane-operations per second (the fp32 vector 157.3 TFLOP/s counts a packed
 # FMA, 4 flops, per lane-operation)
-PEAK_VALU_TSLOTS = 256 * 64 * 2.4e9 / 1e12
+# fp32 vector issue slots: 256 CUs x 128 lane-slots per clock x 2.4 GHz, the
+# chip's published fp32 vector peak (157.3 TFLOP/s) counted one FMA per slot.
+# Measured on the card: a stream of non-packed v_mul_f32 / v_fma_f32 issues
+# about 108 lane-ops per clock per CU once two or more waves share a SIMD (one
+# wave alone: about 51), and v_exp_f32 / v_rcp_f32 about 31, i.e. four slots.
+PEAK_VALU_TSLOTS = 256 * 128 * 2.4e9 / 1e12
 PEAK_F32_MATRIX_TFLOPS = 157.3  # MI355X dense fp32 matrix-core peak
 
 

@@ -36,7 +36,7 @@ template <class Cell, int C>
 struct FusedCfg;
 template <> struct FusedCfg<GruCell, 2> { static constexpr int T = 12, W = 4, LL = 2, OCC = 2; static constexpr bool UKEEP = true; };
 template <> struct FusedCfg<GruCell, 1> { static constexpr int T = 16, W = 4, LL = 1, OCC = 2; static constexpr bool UKEEP = true; };
-template <> struct FusedCfg<LstmCell, 1> { static constexpr int T = 10, W = 4, LL = 1, OCC = 2; static constexpr bool UKEEP = true; };
+template <> struct FusedCfg<LstmCell, 1> { static constexpr int T = 12, W = 4, LL = 2, OCC = 2; static constexpr bool UKEEP = true; };
 
 // Iteration 1 (no state input, lighter cell form): same chunk length and
 // channel tile, its own split into waves and steps.
