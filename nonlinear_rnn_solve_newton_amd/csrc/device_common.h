@@ -132,6 +132,15 @@ struct URaw<float, C> {
     buf_ld_f32<C>(r, voff, soff, v);
   }
   __device__ __forceinline__ float get(int c) const { return v[c]; }
+  // raw bits to / from workgroup memory (C consecutive channels)
+  __device__ __forceinline__ void put_lds(float* q) const {
+#pragma unroll
+    for (int c = 0; c < C; ++c) q[c] = v[c];
+  }
+  __device__ __forceinline__ void get_lds(const float* q) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) v[c] = q[c];
+  }
 };
 
 template <int C>
@@ -166,6 +175,22 @@ struct URaw<bf16, C> {
   }
   __device__ __forceinline__ float get(int c) const {
     return (c & 1) ? bf16_hi(w[c >> 1]) : bf16_lo(w[c >> 1]);
+  }
+  __device__ __forceinline__ void put_lds(bf16* q) const {
+    if constexpr (C == 1) {
+      q->bits = static_cast<uint16_t>(w[0]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NW; ++i) reinterpret_cast<uint32_t*>(q)[i] = w[i];
+    }
+  }
+  __device__ __forceinline__ void get_lds(const bf16* q) {
+    if constexpr (C == 1) {
+      w[0] = q->bits;
+    } else {
+#pragma unroll
+      for (int i = 0; i < NW; ++i) w[i] = reinterpret_cast<const uint32_t*>(q)[i];
+    }
   }
 };
 

@@ -36,8 +36,10 @@
 //   - per-wave maxima of |d| leave through a cross-lane (DPP) reduction, one
 //     word per wave, reduced over the grid by the finalize launch.
 //
-// UKEEP: keep the gate inputs in registers for all iterations (one HBM read
-// per solve) or stream them again in every iteration (fewer registers).
+// UMODE: where the gate inputs live between iterations. 0: streamed from
+// memory again in every iteration; 1: kept in registers (one HBM read per
+// solve); 2: read once and kept in workgroup memory, each wave in a region of
+// its own (one HBM read per solve, and the registers go to occupancy).
 #pragma once
 
 #include "newton_iter.h"
@@ -69,13 +71,18 @@ __device__ __forceinline__ uint32_t wave_max_bits(uint32_t v) {
   return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
 }
 
-template <class Cell, class UT, int C, int T, int W, int LL, int OCC, bool UKEEP>
+template <class Cell, class UT, int C, int T, int W, int LL, int OCC, int UMODE>
 __global__ void __launch_bounds__(64 * W, OCC) newton_fused_kernel(const FusedArgs p) {
   constexpr int NS = Cell::NS, G = Cell::G;
   constexpr int LD = 64 / LL, CW = LD * C, CL = W * LL * T, NA = NS * NS + NS;
   constexpr int TPOLL = T / 2;  // the predecessor's carry is read before this step
 
   __shared__ float s_agg[2][W][NA][CW];  // per-wave aggregates, double-buffered over iterations
+  // UMODE 2: gate inputs [wave][lane group][step][gate][channel], one padding
+  // segment per lane group so the lane groups of a wave read disjoint banks
+  constexpr int USEG = LD * C;  // elements of one (step, gate) row of a lane group
+  constexpr int UGRP = T * G * USEG + USEG;
+  __shared__ __align__(16) UT s_u[UMODE == 2 ? W * LL * UGRP : 1];
   __shared__ unsigned int s_ticket;
 
   const int tid = threadIdx.x;
@@ -122,12 +129,22 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_fused_kernel(const FusedAr
   float av[G][C];
 #pragma unroll
   for (int g = 0; g < G; ++g) ld_f32<C>(p.a + static_cast<long long>(g) * p.D + dc, av[g]);
-  URaw<UT, C> uu[UKEEP ? T : 1][G];
-  if constexpr (UKEEP) {
+  URaw<UT, C> uu[UMODE == 1 ? T : 1][G];
+  UT* su = s_u + (wave * LL + ll) * UGRP + ld * C;  // this lane's channels, step 0, gate 0
+  if constexpr (UMODE == 1) {
 #pragma unroll
     for (int t = 0; t < T; ++t)
 #pragma unroll
       for (int g = 0; g < G; ++g) uu[t][g].load(ru, vu0 + t * ustep, static_cast<uint32_t>(g) * gstep);
+  } else if constexpr (UMODE == 2) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      URaw<UT, C> x[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) x[g].load(ru, vu0 + t * ustep, static_cast<uint32_t>(g) * gstep);
+#pragma unroll
+      for (int g = 0; g < G; ++g) x[g].put_lds(su + (t * G + g) * USEG);
+    }
   }
   // iterate k-1 at the lane's steps (S^(0) = 0), and at the row before the
   // lane group's first step (the fixed initial state before the sequence)
@@ -178,7 +195,8 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_fused_kernel(const FusedAr
       URaw<UT, C> ut[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        if constexpr (UKEEP) ut[g] = uu[t][g];
+        if constexpr (UMODE == 1) ut[g] = uu[t][g];
+        else if constexpr (UMODE == 2) ut[g].get_lds(su + (t * G + g) * USEG);
         else ut[g].load(ru, vu0 + t * ustep, static_cast<uint32_t>(g) * gstep);
       }
 #pragma unroll

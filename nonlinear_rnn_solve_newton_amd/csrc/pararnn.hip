@@ -31,12 +31,13 @@ template <> struct Cfg<GruCell, 2, true> { static constexpr int T = 8, W = 4, LL
 template <> struct Cfg<GruCell, 1, true> { static constexpr int T = 8, W = 8, LL = 2, OCC = 2; };
 template <> struct Cfg<LstmCell, 1, true> { static constexpr int T = 16, W = 4, LL = 1, OCC = 2; };
 // All K iterations in one launch (newton_fused.h): the iterate stays in
-// registers between iterations; UKEEP also keeps the gate inputs there.
+// registers between iterations; UMODE says where the gate inputs stay (1:
+// registers, 2: workgroup memory).
 template <class Cell, int C>
 struct FusedCfg;
-template <> struct FusedCfg<GruCell, 2> { static constexpr int T = 12, W = 4, LL = 2, OCC = 2; static constexpr bool UKEEP = true; };
-template <> struct FusedCfg<GruCell, 1> { static constexpr int T = 16, W = 4, LL = 1, OCC = 2; static constexpr bool UKEEP = true; };
-template <> struct FusedCfg<LstmCell, 1> { static constexpr int T = 12, W = 4, LL = 2, OCC = 2; static constexpr bool UKEEP = true; };
+template <> struct FusedCfg<GruCell, 2> { static constexpr int T = 14, W = 4, LL = 4, OCC = 3; static constexpr int UMODE = 2; };
+template <> struct FusedCfg<GruCell, 1> { static constexpr int T = 16, W = 4, LL = 1, OCC = 2; static constexpr int UMODE = 1; };
+template <> struct FusedCfg<LstmCell, 1> { static constexpr int T = 12, W = 4, LL = 2, OCC = 2; static constexpr int UMODE = 1; };
 
 // Iteration 1 (no state input, lighter cell form): same chunk length and
 // channel tile, its own split into waves and steps.
@@ -355,7 +356,7 @@ int launch_fused(const FusedArgs& a, hipStream_t s) {
   using K = FusedCfg<Cell, C>;
   const unsigned grid = static_cast<unsigned>(a.B) * a.ntiles_d * static_cast<unsigned>(a.nchunks);
   const FusedArgs& b = a;
-  hipLaunchKernelGGL((newton_fused_kernel<Cell, UT, C, K::T, K::W, K::LL, K::OCC, K::UKEEP>), dim3(grid),
+  hipLaunchKernelGGL((newton_fused_kernel<Cell, UT, C, K::T, K::W, K::LL, K::OCC, K::UMODE>), dim3(grid),
                      dim3(64 * K::W), 0, s, b);
   return check_hip(hipGetLastError());
 }
