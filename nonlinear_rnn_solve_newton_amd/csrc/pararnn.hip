@@ -37,7 +37,7 @@ template <class Cell, int C>
 struct FusedCfg;
 template <> struct FusedCfg<GruCell, 2> { static constexpr int T = 14, W = 4, LL = 4, OCC = 3; static constexpr int UMODE = 2; };
 template <> struct FusedCfg<GruCell, 1> { static constexpr int T = 16, W = 4, LL = 1, OCC = 2; static constexpr int UMODE = 1; };
-template <> struct FusedCfg<LstmCell, 1> { static constexpr int T = 12, W = 4, LL = 2, OCC = 2; static constexpr int UMODE = 1; };
+template <> struct FusedCfg<LstmCell, 1> { static constexpr int T = 10, W = 4, LL = 2, OCC = 3; static constexpr int UMODE = 2; };
 
 // Iteration 1 (no state input, lighter cell form): same chunk length and
 // channel tile, its own split into waves and steps.
@@ -354,9 +354,11 @@ bool use_fused(const pararnn_opts* o) {
 template <class Cell, class UT, int C>
 int launch_fused(const FusedArgs& a, hipStream_t s) {
   using K = FusedCfg<Cell, C>;
+  // fp32 gate inputs would take twice the workgroup memory: stream them instead
+  constexpr int UM = (K::UMODE == 2 && sizeof(UT) > 2) ? 0 : K::UMODE;
   const unsigned grid = static_cast<unsigned>(a.B) * a.ntiles_d * static_cast<unsigned>(a.nchunks);
   const FusedArgs& b = a;
-  hipLaunchKernelGGL((newton_fused_kernel<Cell, UT, C, K::T, K::W, K::LL, K::OCC, K::UMODE>), dim3(grid),
+  hipLaunchKernelGGL((newton_fused_kernel<Cell, UT, C, K::T, K::W, K::LL, K::OCC, UM>), dim3(grid),
                      dim3(64 * K::W), 0, s, b);
   return check_hip(hipGetLastError());
 }
