@@ -7,14 +7,13 @@
 // its iterate in registers from iteration to iteration; the intermediate
 // iterates never reach HBM, and only the K-th is stored. Iteration k is the
 // update form of the one-launch kernel (newton_iter.h): d_l = J_l d_{l-1} + r_l
-// with r_l = f(S^(k-1)_{l-1}, u_l) - S^(k-1)_l. What crosses lane, wave and
-// workgroup boundaries between iterations is the iterate at the row before a
-// lane's first step:
-//   - inside a workgroup, the previous lane group's last state, through LDS;
-//   - at the chunk boundary, S^(k)_{c CL - 1}, which the workgroup builds from
-//     its own carry-ins: the carry entering the chunk in iteration k is
-//     exactly d^(k) at that row, so S^(k) = S^(k-1) + carry_k there (S^(0) = 0;
-//     the first chunk sees the fixed initial state).
+// with r_l = f(S^(k-1)_{l-1}, u_l) - S^(k-1)_l. The one value a lane needs
+// from outside its own steps is the iterate at the row before its first step,
+// its linearisation point there. The carry entering the lane group in
+// iteration k is exactly the update d^(k) at that row, so each lane keeps that
+// iterate as a running sum, S^(k) = S^(k-1) + carry_k (S^(0) = 0; the first
+// lane group of the first chunk sees the fixed initial state), and nothing
+// crosses lanes, waves or workgroups for it.
 // Every iteration has its own descriptor slots, so a predecessor that runs
 // ahead never overwrites what a later chunk still has to read; workgroups
 // take tickets in chunk-major order and only ever wait for earlier tickets,
@@ -30,9 +29,6 @@
 //   - each wave forms its own carry-in from the chunk carry and the preceding
 //     waves' aggregates, so one barrier per iteration is enough; the last wave
 //     publishes the chunk's inclusive carry;
-//   - the iterate at the row before a lane group's first step, its next
-//     linearisation point, is kept as a running sum: it moves by the carry
-//     entering the lane group (the update d at that row), with no exchange;
 //   - per-wave maxima of |d| leave through a cross-lane (DPP) reduction, one
 //     word per wave, reduced over the grid by the finalize launch.
 //
