@@ -20,6 +20,7 @@ import ctypes
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 from pathlib import Path
@@ -59,9 +60,14 @@ def adjoint_bytes(cell: str, u_bytes: int) -> int:
 
 
 def source_digest() -> str:
+    """Digest of the kernel sources with comments and blank lines removed, so
+    that counters stay tied to the code they were taken on, not its comments."""
     h = hashlib.sha256()
     for p in sorted((ROOT / "nonlinear_rnn_solve_newton_amd" / "csrc").glob("*")):
-        h.update(p.read_bytes())
+        text = re.sub(r"/\*.*?\*/", "", p.read_text(), flags=re.S)
+        lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines())
+        h.update(p.name.encode())
+        h.update("\n".join(ln for ln in lines if ln).encode())
     return h.hexdigest()[:16]
 
 
