@@ -21,12 +21,15 @@ struct bf16 {
 // numerics: logistic sigmoid from the hardware base-2 exponential and
 // reciprocal (about 1 ulp each); tanh(x) = 2 s(2x) - 1. Overflow of the
 // exponential gives the correct limits (s -> 0 or 1); NaN propagates.
-__device__ __forceinline__ float sigm(float x) {
-  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.4426950408889634f));
+constexpr float kSigmScale = -1.4426950408889634f;  // -log2(e)
+constexpr float kTanhScale = -2.8853900817779268f;  // -2 log2(e)
+// the same functions of an argument already multiplied by their scale
+__device__ __forceinline__ float sigm2(float y) { return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(y)); }
+__device__ __forceinline__ float tanh2(float y) {
+  return fmaf(2.0f, __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(y)), -1.0f);
 }
-__device__ __forceinline__ float tanh_fast(float x) {
-  return fmaf(2.0f, __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -2.8853900817779268f)), -1.0f);
-}
+__device__ __forceinline__ float sigm(float x) { return sigm2(x * kSigmScale); }
+__device__ __forceinline__ float tanh_fast(float x) { return tanh2(x * kTanhScale); }
 
 // ---------------------------------------------------------------------------
 // vector loads / stores of C consecutive channels (C in {1, 2, 4}); the host
@@ -207,6 +210,29 @@ struct GruCell {
   static constexpr int NS = 1;  // state: h
   static constexpr int G = 3;   // gates: z, r, c
 
+  // multiplier of each gate's pre-activation inside its base-2 exponential
+  static constexpr float kScale[G] = {kSigmScale, kSigmScale, kTanhScale};
+
+  // next state and Jacobian from the gate values at state h; Z: h = 0, with
+  // the products of the zero state dropped
+  template <bool Z>
+  __device__ static __forceinline__ void assemble(const float (&a)[G], float z, float r, float c, float h,
+                                                  float (&f)[NS], float (&J)[NS][NS]) {
+    const float omz = 1.0f - z;
+    const float gc = z * fmaf(-c, c, 1.0f);    // df / d pre_c
+    if constexpr (Z) {
+      f[0] = z * c;
+      const float gz = c * z * omz;
+      J[0][0] = fmaf(gc * a[2], r, fmaf(gz, a[0], omz));
+    } else {
+      const float cmh = c - h;
+      f[0] = fmaf(z, cmh, h);  // (1 - z) h + z c
+      const float gz = cmh * z * omz;            // df / d pre_z
+      const float drh = fmaf(h * a[1], r - r * r, r);  // d (r h) / dh
+      J[0][0] = fmaf(gc * a[2], drh, fmaf(gz, a[0], omz));
+    }
+  }
+
   __device__ static __forceinline__ void step(const float (&a)[G], const float (&u)[G],
                                               const float (&s)[NS], float (&f)[NS],
                                               float (&J)[NS][NS]) {
@@ -214,13 +240,7 @@ struct GruCell {
     const float z = sigm(fmaf(a[0], h, u[0]));
     const float r = sigm(fmaf(a[1], h, u[1]));
     const float c = tanh_fast(fmaf(a[2], r * h, u[2]));
-    const float cmh = c - h;
-    f[0] = fmaf(z, cmh, h);  // (1 - z) h + z c
-    const float omz = 1.0f - z;
-    const float gz = cmh * z * omz;            // df / d pre_z
-    const float gc = z * fmaf(-c, c, 1.0f);    // df / d pre_c
-    const float drh = fmaf(h * a[1], r - r * r, r);  // d (r h) / dh
-    J[0][0] = fmaf(gc * a[2], drh, fmaf(gz, a[0], omz));
+    assemble<false>(a, z, r, c, h, f, J);
   }
 
   // step() at the zero state h = 0, with the products of the zero state
@@ -228,14 +248,22 @@ struct GruCell {
   // (a * 0 is then a signed zero that the following add absorbs).
   __device__ static __forceinline__ void step_zero(const float (&a)[G], const float (&u)[G],
                                                    float (&f)[NS], float (&J)[NS][NS]) {
-    const float z = sigm(u[0]);
-    const float r = sigm(u[1]);
-    const float c = tanh_fast(u[2]);
-    f[0] = z * c;
-    const float omz = 1.0f - z;
-    const float gz = c * z * omz;
-    const float gc = z * fmaf(-c, c, 1.0f);
-    J[0][0] = fmaf(gc * a[2], r, fmaf(gz, a[0], omz));
+    assemble<true>(a, sigm(u[0]), sigm(u[1]), tanh_fast(u[2]), 0.0f, f, J);
+  }
+
+  // step() and step_zero() with the coefficients and inputs already multiplied
+  // by kScale (as, us), a keeping the plain coefficients for the Jacobian
+  __device__ static __forceinline__ void step_scaled(const float (&a)[G], const float (&as)[G], const float (&us)[G],
+                                                     const float (&s)[NS], float (&f)[NS], float (&J)[NS][NS]) {
+    const float h = s[0];
+    const float z = sigm2(fmaf(as[0], h, us[0]));
+    const float r = sigm2(fmaf(as[1], h, us[1]));
+    const float c = tanh2(fmaf(as[2], r * h, us[2]));
+    assemble<false>(a, z, r, c, h, f, J);
+  }
+  __device__ static __forceinline__ void step_zero_scaled(const float (&a)[G], const float (&us)[G],
+                                                          float (&f)[NS], float (&J)[NS][NS]) {
+    assemble<true>(a, sigm2(us[0]), sigm2(us[1]), tanh2(us[2]), 0.0f, f, J);
   }
 
   static constexpr int NK = 4;  // dh'/du_z, dh'/du_r, dh'/du_c, r h
@@ -275,51 +303,61 @@ struct LstmCell {
   static constexpr int NS = 2;  // state: (c, h)
   static constexpr int G = 4;   // gates: i, f, o, g
 
-  __device__ static __forceinline__ void step(const float (&a)[G], const float (&u)[G],
-                                              const float (&s)[NS], float (&f)[NS],
-                                              float (&J)[NS][NS]) {
-    const float cp = s[0], hp = s[1];
-    const float gi = sigm(fmaf(a[0], hp, u[0]));
-    const float gf = sigm(fmaf(a[1], hp, u[1]));
-    const float go = sigm(fmaf(a[2], hp, u[2]));
-    const float gg = tanh_fast(fmaf(a[3], hp, u[3]));
-    const float cn = fmaf(gf, cp, gi * gg);
+  // multiplier of each gate's pre-activation inside its base-2 exponential
+  static constexpr float kScale[G] = {kSigmScale, kSigmScale, kSigmScale, kTanhScale};
+
+  // next state and Jacobian from the gate values at previous cell state cp;
+  // Z: the zero state, with its products dropped
+  template <bool Z>
+  __device__ static __forceinline__ void assemble(const float (&a)[G], float gi, float gf, float go, float gg,
+                                                  float cp, float (&f)[NS], float (&J)[NS][NS]) {
+    const float cn = Z ? gi * gg : fmaf(gf, cp, gi * gg);
     const float t = tanh_fast(cn);
     f[0] = cn;
     f[1] = go * t;
     const float dci = gg * (gi - gi * gi);
-    const float dcf = cp * (gf - gf * gf);
     const float dcg = gi * fmaf(-gg, gg, 1.0f);
     const float q = go * fmaf(-t, t, 1.0f);  // dh'/dc'
     const float dho = t * (go - go * go);
-    const float X = fmaf(dci, a[0], fmaf(dcf, a[1], dcg * a[3]));  // dc'/dh
+    float X;  // dc'/dh
+    if constexpr (Z) {
+      X = fmaf(dci, a[0], dcg * a[3]);
+    } else {
+      const float dcf = cp * (gf - gf * gf);
+      X = fmaf(dci, a[0], fmaf(dcf, a[1], dcg * a[3]));
+    }
     J[0][0] = gf;
     J[0][1] = X;
     J[1][0] = q * gf;
     J[1][1] = fmaf(dho, a[2], q * X);
   }
 
+  __device__ static __forceinline__ void step(const float (&a)[G], const float (&u)[G],
+                                              const float (&s)[NS], float (&f)[NS],
+                                              float (&J)[NS][NS]) {
+    const float hp = s[1];
+    assemble<false>(a, sigm(fmaf(a[0], hp, u[0])), sigm(fmaf(a[1], hp, u[1])), sigm(fmaf(a[2], hp, u[2])),
+                    tanh_fast(fmaf(a[3], hp, u[3])), s[0], f, J);
+  }
+
   // step() at the zero state (c, h) = 0, with the products of the zero state
   // dropped: equal to step(a, u, {0, 0}) bit for bit when every a is finite.
   __device__ static __forceinline__ void step_zero(const float (&a)[G], const float (&u)[G],
                                                    float (&f)[NS], float (&J)[NS][NS]) {
-    const float gi = sigm(u[0]);
-    const float gf = sigm(u[1]);
-    const float go = sigm(u[2]);
-    const float gg = tanh_fast(u[3]);
-    const float cn = gi * gg;
-    const float t = tanh_fast(cn);
-    f[0] = cn;
-    f[1] = go * t;
-    const float dci = gg * (gi - gi * gi);
-    const float dcg = gi * fmaf(-gg, gg, 1.0f);
-    const float q = go * fmaf(-t, t, 1.0f);
-    const float dho = t * (go - go * go);
-    const float X = fmaf(dci, a[0], dcg * a[3]);
-    J[0][0] = gf;
-    J[0][1] = X;
-    J[1][0] = q * gf;
-    J[1][1] = fmaf(dho, a[2], q * X);
+    assemble<true>(a, sigm(u[0]), sigm(u[1]), sigm(u[2]), tanh_fast(u[3]), 0.0f, f, J);
+  }
+
+  // step() and step_zero() with the coefficients and inputs already multiplied
+  // by kScale (as, us), a keeping the plain coefficients for the Jacobian
+  __device__ static __forceinline__ void step_scaled(const float (&a)[G], const float (&as)[G], const float (&us)[G],
+                                                     const float (&s)[NS], float (&f)[NS], float (&J)[NS][NS]) {
+    const float hp = s[1];
+    assemble<false>(a, sigm2(fmaf(as[0], hp, us[0])), sigm2(fmaf(as[1], hp, us[1])),
+                    sigm2(fmaf(as[2], hp, us[2])), tanh2(fmaf(as[3], hp, us[3])), s[0], f, J);
+  }
+  __device__ static __forceinline__ void step_zero_scaled(const float (&a)[G], const float (&us)[G],
+                                                          float (&f)[NS], float (&J)[NS][NS]) {
+    assemble<true>(a, sigm2(us[0]), sigm2(us[1]), sigm2(us[2]), tanh2(us[3]), 0.0f, f, J);
   }
 
   // q = dh'/dc', then dc'/du_i, dc'/du_f, dc'/du_g and dh'/du_o; the input

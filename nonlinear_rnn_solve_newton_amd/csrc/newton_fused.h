@@ -35,7 +35,10 @@
 // UMODE: where the gate inputs live between iterations. 0: streamed from
 // memory again in every iteration; 1: kept in registers (one HBM read per
 // solve); 2: read once and kept in workgroup memory, each wave in a region of
-// its own (one HBM read per solve, and the registers go to occupancy).
+// its own (one HBM read per solve, and the registers go to occupancy); 3: as
+// 2, but widened to fp32 and multiplied by the cell's exponential scales on
+// the way in, so that no iteration widens or scales them again (twice the
+// workgroup memory of 2 for bf16 inputs).
 #pragma once
 
 #include "newton_iter.h"
@@ -79,6 +82,7 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_fused_kernel(const FusedAr
   constexpr int USEG = LD * C;  // elements of one (step, gate) row of a lane group
   constexpr int UGRP = T * G * USEG + USEG;
   __shared__ __align__(16) UT s_u[UMODE == 2 ? W * LL * UGRP : 1];
+  __shared__ __align__(16) float s_us[UMODE == 3 ? W * LL * UGRP : 1];  // UMODE 3: scaled fp32
   __shared__ unsigned int s_ticket;
 
   const int tid = threadIdx.x;
@@ -127,6 +131,14 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_fused_kernel(const FusedAr
   for (int g = 0; g < G; ++g) ld_f32<C>(p.a + static_cast<long long>(g) * p.D + dc, av[g]);
   URaw<UT, C> uu[UMODE == 1 ? T : 1][G];
   UT* su = s_u + (wave * LL + ll) * UGRP + ld * C;  // this lane's channels, step 0, gate 0
+  float* sus = s_us + (wave * LL + ll) * UGRP + ld * C;
+  float avs[UMODE == 3 ? G : 1][C];  // coefficients times the exponential scales
+  if constexpr (UMODE == 3) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int c = 0; c < C; ++c) avs[g][c] = av[g][c] * Cell::kScale[g];
+  }
   if constexpr (UMODE == 1) {
 #pragma unroll
     for (int t = 0; t < T; ++t)
@@ -140,6 +152,17 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_fused_kernel(const FusedAr
       for (int g = 0; g < G; ++g) x[g].load(ru, vu0 + t * ustep, static_cast<uint32_t>(g) * gstep);
 #pragma unroll
       for (int g = 0; g < G; ++g) x[g].put_lds(su + (t * G + g) * USEG);
+    }
+  } else if constexpr (UMODE == 3) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      URaw<UT, C> x[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) x[g].load(ru, vu0 + t * ustep, static_cast<uint32_t>(g) * gstep);
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int c = 0; c < C; ++c) sus[(t * G + g) * USEG + c] = x[g].get(c) * Cell::kScale[g];
     }
   }
   // iterate k-1 at the lane's steps (S^(0) = 0), and at the row before the
@@ -189,21 +212,35 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_fused_kernel(const FusedAr
         __builtin_amdgcn_sched_barrier(0);
       }
       URaw<UT, C> ut[G];
+      float uts[UMODE == 3 ? G : 1][C];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         if constexpr (UMODE == 1) ut[g] = uu[t][g];
         else if constexpr (UMODE == 2) ut[g].get_lds(su + (t * G + g) * USEG);
-        else ut[g].load(ru, vu0 + t * ustep, static_cast<uint32_t>(g) * gstep);
+        else if constexpr (UMODE == 3) {
+#pragma unroll
+          for (int c = 0; c < C; ++c) uts[g][c] = sus[(t * G + g) * USEG + c];
+        } else {
+          ut[g].load(ru, vu0 + t * ustep, static_cast<uint32_t>(g) * gstep);
+        }
       }
 #pragma unroll
       for (int c = 0; c < C; ++c) {
         float ac[G], uc[G], pc[NS], f[NS], J[NS][NS];
 #pragma unroll
-        for (int g = 0; g < G; ++g) { ac[g] = av[g][c]; uc[g] = ut[g].get(c); }
+        for (int g = 0; g < G; ++g) { ac[g] = av[g][c]; uc[g] = UMODE == 3 ? uts[g][c] : ut[g].get(c); }
 #pragma unroll
         for (int s = 0; s < NS; ++s) pc[s] = (t == 0) ? sp[s][c] : so[t - 1][s][c];
-        if (ZERO && t > 1) Cell::step_zero(ac, uc, f, J);
-        else Cell::step(ac, uc, pc, f, J);
+        if constexpr (UMODE == 3) {
+          float acs[G];
+#pragma unroll
+          for (int g = 0; g < G; ++g) acs[g] = avs[g][c];
+          if (ZERO && t > 1) Cell::step_zero_scaled(ac, uc, f, J);
+          else Cell::step_scaled(ac, acs, uc, pc, f, J);
+        } else {
+          if (ZERO && t > 1) Cell::step_zero(ac, uc, f, J);
+          else Cell::step(ac, uc, pc, f, J);
+        }
 #pragma unroll
         for (int r = 0; r < NS; ++r) {
 #pragma unroll
