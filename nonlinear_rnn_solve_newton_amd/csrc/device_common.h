@@ -210,9 +210,6 @@ struct GruCell {
   static constexpr int NS = 1;  // state: h
   static constexpr int G = 3;   // gates: z, r, c
 
-  // multiplier of each gate's pre-activation inside its base-2 exponential
-  static constexpr float kScale[G] = {kSigmScale, kSigmScale, kTanhScale};
-
   // next state and Jacobian from the gate values at state h; Z: h = 0, with
   // the products of the zero state dropped
   template <bool Z>
@@ -251,20 +248,6 @@ struct GruCell {
     assemble<true>(a, sigm(u[0]), sigm(u[1]), tanh_fast(u[2]), 0.0f, f, J);
   }
 
-  // step() and step_zero() with the coefficients and inputs already multiplied
-  // by kScale (as, us), a keeping the plain coefficients for the Jacobian
-  __device__ static __forceinline__ void step_scaled(const float (&a)[G], const float (&as)[G], const float (&us)[G],
-                                                     const float (&s)[NS], float (&f)[NS], float (&J)[NS][NS]) {
-    const float h = s[0];
-    const float z = sigm2(fmaf(as[0], h, us[0]));
-    const float r = sigm2(fmaf(as[1], h, us[1]));
-    const float c = tanh2(fmaf(as[2], r * h, us[2]));
-    assemble<false>(a, z, r, c, h, f, J);
-  }
-  __device__ static __forceinline__ void step_zero_scaled(const float (&a)[G], const float (&us)[G],
-                                                          float (&f)[NS], float (&J)[NS][NS]) {
-    assemble<true>(a, sigm2(us[0]), sigm2(us[1]), tanh2(us[2]), 0.0f, f, J);
-  }
 
   static constexpr int NK = 4;  // dh'/du_z, dh'/du_r, dh'/du_c, r h
   __device__ static __forceinline__ void step_adj(const float (&a)[G], const float (&u)[G],
