@@ -166,9 +166,12 @@ bool opts_ok(int cell, int op, const pararnn_opts* o) {
   const double n = static_cast<double>(o->B) * o->L * o->D * 4;
   if (n > 9.0e18) return false;
   for (int C = 1; C <= cmax_for(cell, op); C *= 2) {
-    const Geo g = geo_for(cell, op, C);
-    const double wgs = static_cast<double>(o->B) * ((o->D + g.cw - 1) / g.cw) * ((o->L + g.chunk - 1) / g.chunk);
-    if (wgs > 2.0e9) return false;
+    // both schedules of the solve: the per-iteration and the fused geometry
+    for (int fused = 0; fused <= (op == PARARNN_OP_SOLVE ? 1 : 0); ++fused) {
+      const Geo g = fused ? fused_geo_for(cell, C) : geo_for(cell, op, C);
+      const double wgs = static_cast<double>(o->B) * ((o->D + g.cw - 1) / g.cw) * ((o->L + g.chunk - 1) / g.chunk);
+      if (wgs > 2.0e9) return false;
+    }
   }
   return true;
 }
