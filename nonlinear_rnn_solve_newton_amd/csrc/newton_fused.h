@@ -165,6 +165,10 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_fused_kernel(const FusedAr
         for (int c = 0; c < C; ++c) sus[(t * G + g) * USEG + c] = x[g].get(c) * Cell::kScale[g];
     }
   }
+  // every iteration, the first included, reads the inputs back from workgroup
+  // memory: the compiler may not keep the just-stored values in registers
+  // instead, which would hold them live through the first iteration
+  if constexpr (UMODE >= 2) __asm__ volatile("" ::: "memory");
   // iterate k-1 at the lane's steps (S^(0) = 0), and at the row before the
   // lane group's first step (the fixed initial state before the sequence)
   float so[T][NS][C];

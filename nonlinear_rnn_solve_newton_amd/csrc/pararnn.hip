@@ -36,9 +36,9 @@ template <> struct Cfg<LstmCell, 1, true> { static constexpr int T = 16, W = 4, 
 // pre-scaled for the exponentials).
 template <class Cell, int C>
 struct FusedCfg;
-template <> struct FusedCfg<GruCell, 2> { static constexpr int T = 14, W = 4, LL = 4, OCC = 3; static constexpr int UMODE = 2; };
+template <> struct FusedCfg<GruCell, 2> { static constexpr int T = 16, W = 4, LL = 4, OCC = 3; static constexpr int UMODE = 2; };
 template <> struct FusedCfg<GruCell, 1> { static constexpr int T = 16, W = 4, LL = 1, OCC = 2; static constexpr int UMODE = 1; };
-template <> struct FusedCfg<LstmCell, 1> { static constexpr int T = 9, W = 4, LL = 2, OCC = 3; static constexpr int UMODE = 3; };
+template <> struct FusedCfg<LstmCell, 1> { static constexpr int T = 11, W = 4, LL = 2, OCC = 3; static constexpr int UMODE = 3; };
 
 // Iteration 1 (no state input, lighter cell form): same chunk length and
 // channel tile, its own split into waves and steps.
