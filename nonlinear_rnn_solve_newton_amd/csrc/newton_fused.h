@@ -202,17 +202,14 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_fused_kernel(const FusedAr
     for (int t = 0; t < T; ++t) {
       if (t == TPOLL) {
         __builtin_amdgcn_sched_barrier(0);
+        // every workgroup issues the read, so that no branch hides it from
+        // the compiler's count of loads in flight; the first chunk reads its
+        // own slot and ignores the value
+        const long long pc = pred ? chunk - 1 : 0;
 #pragma unroll
         for (int s = 0; s < NS; ++s)
 #pragma unroll
-          for (int c = 0; c < C; ++c) early[s][c] = 0ull;
-        if (pred) {
-#pragma unroll
-          for (int s = 0; s < NS; ++s)
-#pragma unroll
-            for (int c = 0; c < C; ++c)
-              early[s][c] = desc_get(incl + (static_cast<long long>(chunk - 1) * NS + s) * BD + chan + c * LD);
-        }
+          for (int c = 0; c < C; ++c) early[s][c] = desc_get(incl + (pc * NS + s) * BD + chan + c * LD);
         __builtin_amdgcn_sched_barrier(0);
       }
       URaw<UT, C> ut[G];
@@ -277,6 +274,13 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_fused_kernel(const FusedAr
         }
     }
     __syncthreads();
+    // the early read completes here on every path: one still in flight
+    // past the branches below would make the compiler wait for all memory
+    // operations at the next iteration's start, the stores included
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int c = 0; c < C; ++c) __asm__ volatile("" ::"v"(early[s][c]));
 
     auto wave_agg = [&](int w) {
       Aff<NS, C> e;

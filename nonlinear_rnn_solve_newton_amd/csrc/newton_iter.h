@@ -76,6 +76,14 @@ __device__ __forceinline__ void lookback(unsigned long long* incl, unsigned long
     for (int q = 0; q < NA; ++q)
 #pragma unroll
       for (int c = 0; c < C; ++c) wa[q][c] = desc_get(agg + ((long long)i * NA + q) * BD + chan + c * cs);
+    // both reads complete here, also where only the first is used: a read
+    // left in flight past the return makes the compiler wait for every
+    // memory operation (stores included) at the caller's next use of its
+    // registers
+#pragma unroll
+    for (int q = 0; q < NA; ++q)
+#pragma unroll
+      for (int c = 0; c < C; ++c) __asm__ volatile("" ::"v"(wa[q][c]));
     bool ok_i = true, ok_a = true;
 #pragma unroll
     for (int s = 0; s < NS; ++s)

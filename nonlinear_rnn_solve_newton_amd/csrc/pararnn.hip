@@ -198,7 +198,9 @@ Layout layout(int cell, int op, const pararnn_opts* o, bool with_da, Geo g, bool
   y.incl = off;
   const size_t slots = B * static_cast<size_t>(y.ntiles_d) * g.cw;  // descriptor slots per component
   const size_t nk = fused ? static_cast<size_t>(K) : 1;  // descriptor sets
-  if (y.nchunks > 1) off = round_up(off + sizeof(uint64_t) * nk * y.nchunks * NS * slots);
+  // the fused kernel reads a descriptor slot in every workgroup, a single
+  // chunk included
+  if (y.nchunks > 1 || fused) off = round_up(off + sizeof(uint64_t) * nk * y.nchunks * NS * slots);
   y.agg = off;
   if (y.nchunks > 1) off = round_up(off + sizeof(uint64_t) * nk * y.nchunks * (NS * NS + NS) * slots);
   y.zero_end = off;
