@@ -82,11 +82,18 @@ typedef struct {
   int32_t early_exit; /* 0: always K iterations. 1: stop after the first iteration
                          whose update satisfies tol on every row (later launches copy) */
   int32_t u_dtype;    /* pararnn_dtype of u */
-  void* const* events; /* optional: K + 2 hipEvent_t handles recorded on `stream`
-                          before the workspace reset, after it, and after each
-                          iteration (solve; with the fused schedule all K after
-                          its one launch) / the adjoint launch (adjoint: 3
-                          events); NULL = none */
+  void* const* events; /* optional, NULL = none: hipEvent_t handles, each NULL
+                          or created by the caller. Solve (K + 2): [0] before
+                          the workspace reset; [1] the start of the first
+                          kernel after it; [k + 1] the end of iteration k's
+                          launch (fused schedule: [2] the end of its one
+                          launch, [3..K+1] recorded right after). Adjoint and
+                          scans (3): before the workspace reset (the dense
+                          scan has none), the start of the first kernel, the
+                          end of the last. Starts and ends are
+                          stamped by the kernel dispatch itself, so an
+                          interval between them is execution time without
+                          the latency of a separate marker. */
   int32_t schedule;    /* pararnn_schedule of a solve; ignored by the other calls */
 } pararnn_opts;
 
@@ -144,9 +151,8 @@ int32_t pararnn_adjoint(int32_t cell, const void* u, const float* a, const float
  *   A  [NS*NS][B][L][D], block entries row-major: A00, A01, A10, A11
  *   b  [NS][B][L][D],  s (output) [NS][B][L][D],  s0 [NS][B][D] or NULL.
  * Workspace: pararnn_workspace_bytes(any cell, PARARNN_OP_SCAN_DIAG or
- * PARARNN_OP_SCAN_BLOCK2, o). opts: B, L, D and events (3 handles: before
- * the workspace reset, after it, after the scan) are used; the others are
- * ignored. Non-finite coefficients propagate like any other value. Errors as
+ * PARARNN_OP_SCAN_BLOCK2, o). opts: B, L, D and events (3 handles, as for
+ * the adjoint) are used; the others are ignored. Non-finite coefficients propagate like any other value. Errors as
  * for the solves; 16-byte alignment with D divisible by 4 (diag) or 2 (block2)
  * selects the widest accesses. */
 int32_t pararnn_scan_diag(const float* A, const float* b, const float* s0, float* s, void* ws,
@@ -162,7 +168,7 @@ int32_t pararnn_scan_block2(const float* A, const float* b, const float* s0, flo
  *   s_l[r] = sum_q A_l[r][q] s_{l-1}[q] + b_l[r].
  * Layouts (device, fp32, row-major): A [B][L][n][n], b and s (output)
  * [B][L][n], s0 [B][n] or NULL. n = opts.D, 1 <= n <= 32; opts.B and opts.L
- * as usual; opts.events: 3 handles (before, after set-up, after the scan).
+ * as usual; opts.events: 3 handles, as for the adjoint.
  * The chunk transfer products run on the matrix cores in fp32. Workspace:
  * pararnn_workspace_bytes(any cell, PARARNN_OP_SCAN_DENSE, o). Pointers need
  * 4-byte alignment. Errors as for the other calls; n > 32 is EINVAL. */

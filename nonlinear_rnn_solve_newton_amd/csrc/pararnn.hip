@@ -2,6 +2,7 @@
 // argument validation, launch-configuration choice, workspace carving and the
 // launch sequence (workspace reset, then one fused launch per Newton iteration,
 // or one adjoint launch), all asynchronous on the caller's stream.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
@@ -234,6 +235,29 @@ int record(const pararnn_opts* o, int i, hipStream_t s) {
   return check_hip(hipEventRecord(static_cast<hipEvent_t>(o->events[i]), s));
 }
 
+// Caller events that a kernel's own dispatch stamps at its start and end. A
+// marker recorded between two kernels adds its own barrier to the interval
+// it bounds (about 20 us on a 150 us launch); a stamp from the dispatch is
+// the kernel's execution alone.
+struct Stamps {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+Stamps stamps(const pararnn_opts* o, int start, int stop) {
+  Stamps t;
+  if (o->events) {
+    if (start >= 0) t.start = static_cast<hipEvent_t>(o->events[start]);
+    if (stop >= 0) t.stop = static_cast<hipEvent_t>(o->events[stop]);
+  }
+  return t;
+}
+
+template <typename F, typename... Args>
+int launch(F kernel, dim3 grid, dim3 block, hipStream_t s, Stamps t, Args... args) {
+  if (t.start || t.stop) hipExtLaunchKernelGGL(kernel, grid, block, 0, s, t.start, t.stop, 0, args...);
+  else hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+  return check_hip(hipGetLastError());
+}
+
 int clear_ws(char* ws, const Layout& y, float* user, long long nuser, hipStream_t s) {
   const long long n16 = static_cast<long long>(y.zero_end / 16);
   const long long work = n16 > nuser ? n16 : nuser;
@@ -246,7 +270,7 @@ int clear_ws(char* ws, const Layout& y, float* user, long long nuser, hipStream_
 }
 
 template <class Cell, class UT, int C>
-int launch_iter(const IterArgs& a, hipStream_t s) {
+int launch_iter(const IterArgs& a, hipStream_t s, Stamps t) {
   using K = Cfg<Cell, C, false>;
   using K1 = CfgFirst<Cell, C>;
   static_assert(K1::W * K1::LL * K1::T == K::W * K::LL * K::T && K1::LL == K::LL,
@@ -254,62 +278,58 @@ int launch_iter(const IterArgs& a, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>(a.B) * a.ntiles_d * static_cast<unsigned>(a.nchunks);
   const IterArgs& b = a;
   if (a.k == 1)  // iteration 1 starts from the zero iterate and reads no state
-    hipLaunchKernelGGL((newton_iter_kernel<Cell, UT, C, K1::T, K1::W, K1::LL, K1::OCC, true>), dim3(grid),
-                       dim3(64 * K1::W), 0, s, b);
-  else
-    hipLaunchKernelGGL((newton_iter_kernel<Cell, UT, C, K::T, K::W, K::LL, K::OCC, false>), dim3(grid),
-                       dim3(64 * K::W), 0, s, b);
-  return check_hip(hipGetLastError());
+    return launch(newton_iter_kernel<Cell, UT, C, K1::T, K1::W, K1::LL, K1::OCC, true>, dim3(grid),
+                  dim3(64 * K1::W), s, t, b);
+  return launch(newton_iter_kernel<Cell, UT, C, K::T, K::W, K::LL, K::OCC, false>, dim3(grid), dim3(64 * K::W),
+                s, t, b);
 }
 
 template <class Cell, class UT>
-int launch_iter_c(int C, const IterArgs& a, hipStream_t s) {
+int launch_iter_c(int C, const IterArgs& a, hipStream_t s, Stamps t) {
   if constexpr (max_c<Cell, false>() >= 4) {
-    if (C == 4) return launch_iter<Cell, UT, 4>(a, s);
+    if (C == 4) return launch_iter<Cell, UT, 4>(a, s, t);
   }
   if constexpr (max_c<Cell, false>() >= 2) {
-    if (C == 2) return launch_iter<Cell, UT, 2>(a, s);
+    if (C == 2) return launch_iter<Cell, UT, 2>(a, s, t);
   }
-  return launch_iter<Cell, UT, 1>(a, s);
+  return launch_iter<Cell, UT, 1>(a, s, t);
 }
 
 template <class Cell>
-int launch_iter_any(int dtype, int C, const IterArgs& a, hipStream_t s) {
-  return dtype == PARARNN_BF16 ? launch_iter_c<Cell, bf16>(C, a, s) : launch_iter_c<Cell, float>(C, a, s);
+int launch_iter_any(int dtype, int C, const IterArgs& a, hipStream_t s, Stamps t) {
+  return dtype == PARARNN_BF16 ? launch_iter_c<Cell, bf16>(C, a, s, t) : launch_iter_c<Cell, float>(C, a, s, t);
 }
 
 template <class Cell, class UT, int C>
-int launch_adj(const AdjArgs& a, hipStream_t s) {
+int launch_adj(const AdjArgs& a, hipStream_t s, Stamps t) {
   using K = Cfg<Cell, C, true>;
   const unsigned grid = static_cast<unsigned>(a.B) * a.ntiles_d * static_cast<unsigned>(a.nchunks);
   const AdjArgs& b = a;
-  hipLaunchKernelGGL((adjoint_kernel<Cell, UT, C, K::T, K::W, K::LL, K::OCC>), dim3(grid), dim3(64 * K::W), 0, s, b);
-  return check_hip(hipGetLastError());
+  return launch(adjoint_kernel<Cell, UT, C, K::T, K::W, K::LL, K::OCC>, dim3(grid), dim3(64 * K::W), s, t, b);
 }
 
 template <class Cell, class UT>
-int launch_adj_c(int C, const AdjArgs& a, hipStream_t s) {
+int launch_adj_c(int C, const AdjArgs& a, hipStream_t s, Stamps t) {
   if constexpr (max_c<Cell, true>() >= 4) {
-    if (C == 4) return launch_adj<Cell, UT, 4>(a, s);
+    if (C == 4) return launch_adj<Cell, UT, 4>(a, s, t);
   }
   if constexpr (max_c<Cell, true>() >= 2) {
-    if (C == 2) return launch_adj<Cell, UT, 2>(a, s);
+    if (C == 2) return launch_adj<Cell, UT, 2>(a, s, t);
   }
-  return launch_adj<Cell, UT, 1>(a, s);
+  return launch_adj<Cell, UT, 1>(a, s, t);
 }
 
 template <class Cell>
-int launch_adj_any(int dtype, int C, const AdjArgs& a, hipStream_t s) {
-  return dtype == PARARNN_BF16 ? launch_adj_c<Cell, bf16>(C, a, s) : launch_adj_c<Cell, float>(C, a, s);
+int launch_adj_any(int dtype, int C, const AdjArgs& a, hipStream_t s, Stamps t) {
+  return dtype == PARARNN_BF16 ? launch_adj_c<Cell, bf16>(C, a, s, t) : launch_adj_c<Cell, float>(C, a, s, t);
 }
 
 template <int NS, int C>
-int launch_scan(const ScanArgs& a, hipStream_t s) {
+int launch_scan(const ScanArgs& a, hipStream_t s, Stamps t) {
   using K = ScanCfg<NS, C>;
   const unsigned grid = static_cast<unsigned>(a.B) * a.ntiles_d * static_cast<unsigned>(a.nchunks);
   const ScanArgs& b = a;
-  hipLaunchKernelGGL((scan_kernel<NS, C, K::T, K::W, K::LL, K::OCC>), dim3(grid), dim3(64 * K::W), 0, s, b);
-  return check_hip(hipGetLastError());
+  return launch(scan_kernel<NS, C, K::T, K::W, K::LL, K::OCC>, dim3(grid), dim3(64 * K::W), s, t, b);
 }
 
 int scan(int ns, const float* A, const float* b, const float* s0, float* s, void* ws, size_t ws_bytes,
@@ -331,8 +351,6 @@ int scan(int ns, const float* A, const float* b, const float* s0, float* s, void
   if (rc) return rc;
   rc = clear_ws(w, y, nullptr, 0, stream);
   if (rc) return rc;
-  rc = record(o, 1, stream);
-  if (rc) return rc;
   ScanArgs sa;
   memset(&sa, 0, sizeof(sa));
   sa.A = A;
@@ -347,10 +365,9 @@ int scan(int ns, const float* A, const float* b, const float* s0, float* s, void
   sa.D = o->D;
   sa.nchunks = y.nchunks;
   sa.ntiles_d = y.ntiles_d;
-  if (ns == 2) rc = C == 2 ? launch_scan<2, 2>(sa, stream) : launch_scan<2, 1>(sa, stream);
-  else rc = C == 4 ? launch_scan<1, 4>(sa, stream) : C == 2 ? launch_scan<1, 2>(sa, stream) : launch_scan<1, 1>(sa, stream);
-  if (rc) return rc;
-  return record(o, 2, stream);
+  const Stamps t = stamps(o, 1, 2);
+  if (ns == 2) return C == 2 ? launch_scan<2, 2>(sa, stream, t) : launch_scan<2, 1>(sa, stream, t);
+  return C == 4 ? launch_scan<1, 4>(sa, stream, t) : C == 2 ? launch_scan<1, 2>(sa, stream, t) : launch_scan<1, 1>(sa, stream, t);
 }
 
 bool use_fused(const pararnn_opts* o) {
@@ -358,28 +375,27 @@ bool use_fused(const pararnn_opts* o) {
 }
 
 template <class Cell, class UT, int C>
-int launch_fused(const FusedArgs& a, hipStream_t s) {
+int launch_fused(const FusedArgs& a, hipStream_t s, Stamps t) {
   using K = FusedCfg<Cell, C>;
   // fp32 gate inputs would take twice the workgroup memory: stream them instead
   constexpr int UM = (K::UMODE == 2 && sizeof(UT) > 2) ? 0 : K::UMODE;
   const unsigned grid = static_cast<unsigned>(a.B) * a.ntiles_d * static_cast<unsigned>(a.nchunks);
   const FusedArgs& b = a;
-  hipLaunchKernelGGL((newton_fused_kernel<Cell, UT, C, K::T, K::W, K::LL, K::OCC, UM>), dim3(grid),
-                     dim3(64 * K::W), 0, s, b);
-  return check_hip(hipGetLastError());
+  return launch(newton_fused_kernel<Cell, UT, C, K::T, K::W, K::LL, K::OCC, UM>, dim3(grid), dim3(64 * K::W), s,
+                t, b);
 }
 
 template <class Cell, class UT>
-int launch_fused_c(int C, const FusedArgs& a, hipStream_t s) {
+int launch_fused_c(int C, const FusedArgs& a, hipStream_t s, Stamps t) {
   if constexpr (max_c<Cell, false>() >= 2) {
-    if (C == 2) return launch_fused<Cell, UT, 2>(a, s);
+    if (C == 2) return launch_fused<Cell, UT, 2>(a, s, t);
   }
-  return launch_fused<Cell, UT, 1>(a, s);
+  return launch_fused<Cell, UT, 1>(a, s, t);
 }
 
 template <class Cell>
-int launch_fused_any(int dtype, int C, const FusedArgs& a, hipStream_t s) {
-  return dtype == PARARNN_BF16 ? launch_fused_c<Cell, bf16>(C, a, s) : launch_fused_c<Cell, float>(C, a, s);
+int launch_fused_any(int dtype, int C, const FusedArgs& a, hipStream_t s, Stamps t) {
+  return dtype == PARARNN_BF16 ? launch_fused_c<Cell, bf16>(C, a, s, t) : launch_fused_c<Cell, float>(C, a, s, t);
 }
 
 int solve(int cell, const void* u, const float* a, const float* c0, const float* h0, float* c, float* h,
@@ -406,8 +422,6 @@ int solve(int cell, const void* u, const float* a, const float* c0, const float*
     if (rc) return rc;
     rc = clear_ws(static_cast<char*>(ws), y, nullptr, 0, stream);
     if (rc) return rc;
-    rc = record(o, 1, stream);
-    if (rc) return rc;
     char* w = static_cast<char*>(ws);
     FusedArgs fa;
     memset(&fa, 0, sizeof(fa));
@@ -427,10 +441,12 @@ int solve(int cell, const void* u, const float* a, const float* c0, const float*
     fa.K = K;
     fa.nchunks = y.nchunks;
     fa.ntiles_d = y.ntiles_d;
-    rc = (cell == PARARNN_LSTM) ? launch_fused_any<LstmCell>(o->u_dtype, C, fa, stream)
-                                : launch_fused_any<GruCell>(o->u_dtype, C, fa, stream);
+    // the one launch stamps events 1 and 2; iterations 2..K end with it
+    const Stamps t = stamps(o, 1, 2);
+    rc = (cell == PARARNN_LSTM) ? launch_fused_any<LstmCell>(o->u_dtype, C, fa, stream, t)
+                                : launch_fused_any<GruCell>(o->u_dtype, C, fa, stream, t);
     if (rc) return rc;
-    for (int k = 1; k <= K; ++k) {
+    for (int k = 2; k <= K; ++k) {
       rc = record(o, k + 1, stream);
       if (rc) return rc;
     }
@@ -448,8 +464,6 @@ int solve(int cell, const void* u, const float* a, const float* c0, const float*
   int rc = record(o, 0, stream);
   if (rc) return rc;
   rc = clear_ws(w, y, nullptr, 0, stream);
-  if (rc) return rc;
-  rc = record(o, 1, stream);
   if (rc) return rc;
 
   IterArgs ia;
@@ -479,10 +493,10 @@ int solve(int cell, const void* u, const float* a, const float* c0, const float*
       ia.sin[s] = (k == 1) ? nullptr : (k_in_out ? alt[s] : out[s]);
     }
     ia.k = k;
-    rc = (cell == PARARNN_LSTM) ? launch_iter_any<LstmCell>(o->u_dtype, C, ia, stream)
-                                : launch_iter_any<GruCell>(o->u_dtype, C, ia, stream);
-    if (rc) return rc;
-    rc = record(o, k + 1, stream);
+    // launch k stamps event k + 1 at its end (and launch 1 event 1 at its start)
+    const Stamps t = stamps(o, k == 1 ? 1 : -1, k + 1);
+    rc = (cell == PARARNN_LSTM) ? launch_iter_any<LstmCell>(o->u_dtype, C, ia, stream, t)
+                                : launch_iter_any<GruCell>(o->u_dtype, C, ia, stream, t);
     if (rc) return rc;
     if (o->early_exit) {  // the next launch decides from this launch's row maxima
       hipLaunchKernelGGL(rowmax_kernel, dim3(o->B), dim3(kRowmaxThreads), 0, stream, ia.pmax, ia.maxupd, o->B, y.ntiles_d,
@@ -548,13 +562,11 @@ int scan_dense(const float* A, const float* b, const float* s0, float* s, void* 
   const unsigned nwg = static_cast<unsigned>(o->B) * static_cast<unsigned>(y.nchunks);
   int rc = record(o, 0, stream);
   if (rc) return rc;
-  rc = record(o, 1, stream);
-  if (rc) return rc;
-  // n = 32 with 16-byte aligned A reads whole runs of four columns
+  // n = 32 with 16-byte aligned A reads whole runs of four columns; the first
+  // launch stamps event 1 at its start, the last event 2 at its end
   const bool n32 = o->D == 32 && aligned(A, 16);
-  if (n32) hipLaunchKernelGGL(dense_chunk_kernel<true>, dim3(nwg), dim3(64 * kDenseWaves), 0, stream, da);
-  else hipLaunchKernelGGL(dense_chunk_kernel<false>, dim3(nwg), dim3(64 * kDenseWaves), 0, stream, da);
-  rc = check_hip(hipGetLastError());
+  rc = n32 ? launch(dense_chunk_kernel<true>, dim3(nwg), dim3(64 * kDenseWaves), stream, stamps(o, 1, -1), da)
+           : launch(dense_chunk_kernel<false>, dim3(nwg), dim3(64 * kDenseWaves), stream, stamps(o, 1, -1), da);
   if (rc) return rc;
   hipLaunchKernelGGL(dense_carry_kernel, dim3(static_cast<unsigned>(o->B)), dim3(64), 0, stream, da);
   rc = check_hip(hipGetLastError());
@@ -563,11 +575,8 @@ int scan_dense(const float* A, const float* b, const float* s0, float* s, void* 
   rc = check_hip(hipGetLastError());
   if (rc) return rc;
   const unsigned nseg = nwg * kDenseWaves;
-  if (n32) hipLaunchKernelGGL(dense_apply_kernel<true>, dim3(nseg), dim3(64), 0, stream, da);
-  else hipLaunchKernelGGL(dense_apply_kernel<false>, dim3(nseg), dim3(64), 0, stream, da);
-  rc = check_hip(hipGetLastError());
-  if (rc) return rc;
-  return record(o, 2, stream);
+  return n32 ? launch(dense_apply_kernel<true>, dim3(nseg), dim3(64), stream, stamps(o, -1, 2), da)
+             : launch(dense_apply_kernel<false>, dim3(nseg), dim3(64), stream, stamps(o, -1, 2), da);
 }
 
 }  // namespace
@@ -643,8 +652,6 @@ extern "C" int32_t pararnn_adjoint(int32_t cell, const void* u, const float* a, 
   if (rc) return rc;
   rc = clear_ws(w, y, nullptr, 0, stream);
   if (rc) return rc;
-  rc = record(o, 1, stream);
-  if (rc) return rc;
 
   AdjArgs aa;
   memset(&aa, 0, sizeof(aa));
@@ -666,19 +673,19 @@ extern "C" int32_t pararnn_adjoint(int32_t cell, const void* u, const float* a, 
   aa.D = o->D;
   aa.nchunks = y.nchunks;
   aa.ntiles_d = y.ntiles_d;
-  rc = lstm ? launch_adj_any<LstmCell>(o->u_dtype, C, aa, stream)
-            : launch_adj_any<GruCell>(o->u_dtype, C, aa, stream);
+  // the adjoint launch stamps event 1 at its start; event 2 at the end of
+  // the last launch (the da reduction when requested)
+  rc = lstm ? launch_adj_any<LstmCell>(o->u_dtype, C, aa, stream, stamps(o, 1, da ? -1 : 2))
+            : launch_adj_any<GruCell>(o->u_dtype, C, aa, stream, stamps(o, 1, da ? -1 : 2));
   if (rc) return rc;
   if (da) {
     const int G = ngates(cell);
     const long long n = static_cast<long long>(G) * o->D;
-    hipLaunchKernelGGL(da_reduce_kernel, dim3(static_cast<unsigned>((n + kDaCols - 1) / kDaCols)),
-                       dim3(kDaCols * kDaGroups), 0, stream, reinterpret_cast<const float*>(w + y.dapart), da,
-                       y.nchunks * o->B, n);
-    rc = check_hip(hipGetLastError());
-    if (rc) return rc;
+    return launch(da_reduce_kernel, dim3(static_cast<unsigned>((n + kDaCols - 1) / kDaCols)),
+                  dim3(kDaCols * kDaGroups), stream, stamps(o, -1, 2), reinterpret_cast<const float*>(w + y.dapart),
+                  da, y.nchunks * o->B, n);
   }
-  return record(o, 2, stream);
+  return PARARNN_OK;
 }
 
 extern "C" const char* pararnn_strerror(int32_t status) {
