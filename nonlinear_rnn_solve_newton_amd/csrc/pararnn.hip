@@ -568,7 +568,7 @@ int scan_dense(const float* A, const float* b, const float* s0, float* s, void* 
   rc = n32 ? launch(dense_chunk_kernel<true>, dim3(nwg), dim3(64 * kDenseWaves), stream, stamps(o, 1, -1), da)
            : launch(dense_chunk_kernel<false>, dim3(nwg), dim3(64 * kDenseWaves), stream, stamps(o, 1, -1), da);
   if (rc) return rc;
-  hipLaunchKernelGGL(dense_carry_kernel, dim3(static_cast<unsigned>(o->B)), dim3(64), 0, stream, da);
+  hipLaunchKernelGGL(dense_carry_kernel, dim3(static_cast<unsigned>(o->B)), dim3(64 * kDenseCarryWaves), 0, stream, da);
   rc = check_hip(hipGetLastError());
   if (rc) return rc;
   hipLaunchKernelGGL(dense_segcarry_kernel, dim3(nwg), dim3(64), 0, stream, da);

@@ -86,6 +86,18 @@ __device__ __forceinline__ void dense_load_row(const DenseArgs& p, long long ste
   }
 }
 
+// Lanes (i, 0) publish element i of the wave's vector in its LDS slot xl for
+// the next dense_matvec. The LDS operations of one wave complete in order, so
+// the exchange needs no workgroup barrier; the fences and the wave barrier
+// tell the compiler that other lanes wrote the slot. Without them a lane that
+// wrote nothing may keep what it read before, or read before the write.
+__device__ __forceinline__ void dense_share(float* xl, int i, int h, float x) {
+  if (h == 0) xl[i] = x;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // y[i] = sum_q a[i][q] x[q] + bi in lanes i and i + 32, with x[q] read from
 // this wave's LDS vector xl (lane (i, h) reads its four runs of four)
 __device__ __forceinline__ float dense_matvec(const float (&a)[16], const float* xl, int h, float bi) {
@@ -128,7 +140,7 @@ __global__ void __launch_bounds__(64 * kDenseWaves) dense_chunk_kernel(const Den
 #pragma unroll
   for (int r = 0; r < 16; ++r) Q[r] = (dense_row(r, h) == j) ? 1.0f : 0.0f;
   float v = 0.0f;
-  if (h == 0) xl[j] = 0.0f;
+  dense_share(xl, j, h, 0.0f);
   // rows stream through a ring of kDenseRing steps ahead of the chain
   float a[kDenseRing][16], bs[kDenseRing];
 #pragma unroll
@@ -140,7 +152,7 @@ __global__ void __launch_bounds__(64 * kDenseWaves) dense_chunk_kernel(const Den
     if (l_begin + t < l_end) {
       const int k = t % kDenseRing;
       v = dense_matvec(a[k], xl, h, bs[k]);
-      if (h == 0) xl[j] = v;
+      dense_share(xl, j, h, v);
       Q = dense_mfma_chain(a[k], Q);
       if (t + kDenseRing < kDenseSeg && l_begin + t + kDenseRing < l_end)
         dense_load_row<N32>(p, row0 + l_begin + t + kDenseRing, j, h, a[k], bs[k]);
@@ -183,79 +195,118 @@ __global__ void __launch_bounds__(64 * kDenseWaves) dense_chunk_kernel(const Den
   }
 }
 
-// One wave per batch row: carries into every chunk, in order. The chunk
-// transfers stream kDenseCarryAhead chunks ahead of the chain.
-constexpr int kDenseCarryAhead = 4;
-__global__ void __launch_bounds__(64) dense_carry_kernel(const DenseArgs p) {
+// One workgroup per batch row: the carries into every chunk, in order. The
+// chain is one matrix-vector product per chunk; what bounds it is the latency
+// of reading each chunk's transfer. So all waves stage the transfers into LDS
+// a block of kDenseCarryBlock chunks at a time (every load of a block in
+// flight at once), the next block loading while wave 0 runs the chain
+// through the current one. Rows are padded to kDenseCarryRow floats, so the
+// 16-byte row reads of the chain spread over the LDS banks.
+constexpr int kDenseCarryBlock = 16;
+constexpr int kDenseCarryWaves = 4;
+constexpr int kDenseCarryRow = 36;
+constexpr int kDenseCarryPieces = kDenseCarryBlock * 256 / (64 * kDenseCarryWaves);  // f32x4 per thread
+constexpr int kDenseCarryVPieces = kDenseCarryBlock * 32 / (64 * kDenseCarryWaves);  // floats per thread
+__global__ void __launch_bounds__(64 * kDenseCarryWaves) dense_carry_kernel(const DenseArgs p) {
+  __shared__ __align__(16) float s_p[2][kDenseCarryBlock][32 * kDenseCarryRow];
+  __shared__ float s_v[2][kDenseCarryBlock][32];
   __shared__ __align__(16) float xl[32];
-  const int lane = threadIdx.x, j = lane & 31, h = lane >> 5;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, j = lane & 31, h = lane >> 5;
   const int b = blockIdx.x;
   const long long base = static_cast<long long>(b) * p.nchunks;
-  float x = (p.s0 && j < p.n) ? p.s0[static_cast<long long>(b) * p.n + min(j, p.n - 1)] : 0.0f;
-  if (h == 0) xl[j] = x;
-  float ring[kDenseCarryAhead][16], vring[kDenseCarryAhead];
-  auto load = [&](int c, float (&aa)[16], float& vv) {
-    const float* P = p.P + (base + c) * 1024 + j * 32;
+  const int nblk = (p.nchunks + kDenseCarryBlock - 1) / kDenseCarryBlock;
+  f32x4 stage[kDenseCarryPieces];
+  float vstage[kDenseCarryVPieces];
+  // loads of block blk into registers; chunk indices past the end are
+  // clamped onto the last chunk (read, never committed)
+  auto issue = [&](int blk) {
+    const int c0 = blk * kDenseCarryBlock, last = p.nchunks - 1 - c0;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const f32x4 q = *reinterpret_cast<const f32x4*>(P + 8 * g + 4 * h);
-      aa[4 * g] = q.x;
-      aa[4 * g + 1] = q.y;
-      aa[4 * g + 2] = q.z;
-      aa[4 * g + 3] = q.w;
+    for (int i = 0; i < kDenseCarryPieces; ++i) {
+      const int piece = tid + i * 64 * kDenseCarryWaves;
+      const int k = min(piece >> 8, last);
+      stage[i] = *reinterpret_cast<const f32x4*>(p.P + (base + c0 + k) * 1024 + (piece & 255) * 4);
     }
-    vv = p.v[(base + c) * 32 + j];
+#pragma unroll
+    for (int i = 0; i < kDenseCarryVPieces; ++i) {
+      const int e = tid + i * 64 * kDenseCarryWaves;
+      vstage[i] = p.v[(base + c0 + min(e >> 5, last)) * 32 + (e & 31)];
+    }
   };
+  auto commit = [&](int buf) {
 #pragma unroll
-  for (int k = 0; k < kDenseCarryAhead; ++k)
-    if (k < p.nchunks) load(k, ring[k], vring[k]);
-  for (int c0 = 0; c0 < p.nchunks; c0 += kDenseCarryAhead) {
+    for (int i = 0; i < kDenseCarryPieces; ++i) {
+      const int piece = tid + i * 64 * kDenseCarryWaves;
+      const int q = piece & 255;  // row q / 8, columns 4 (q % 8) ..
+      *reinterpret_cast<f32x4*>(&s_p[buf][piece >> 8][(q >> 3) * kDenseCarryRow + (q & 7) * 4]) = stage[i];
+    }
 #pragma unroll
-    for (int k = 0; k < kDenseCarryAhead; ++k) {
-      const int c = c0 + k;
-      if (c < p.nchunks) {
-        if (h == 0) p.carry[(base + c) * 32 + j] = x;
-        x = dense_matvec(ring[k], xl, h, vring[k]);
-        if (h == 0) xl[j] = x;
-        if (c + kDenseCarryAhead < p.nchunks) load(c + kDenseCarryAhead, ring[k], vring[k]);
+    for (int i = 0; i < kDenseCarryVPieces; ++i) {
+      const int e = tid + i * 64 * kDenseCarryWaves;
+      s_v[buf][e >> 5][e & 31] = vstage[i];
+    }
+  };
+  float x = (p.s0 && j < p.n) ? p.s0[static_cast<long long>(b) * p.n + min(j, p.n - 1)] : 0.0f;
+  if (wave == 0 && h == 0) xl[j] = x;
+  issue(0);
+  commit(0);
+  __syncthreads();
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int buf = blk & 1;
+    if (blk + 1 < nblk) issue(blk + 1);
+    if (wave == 0) {
+      const int c0 = blk * kDenseCarryBlock, nc = min(kDenseCarryBlock, p.nchunks - c0);
+      for (int k = 0; k < nc; ++k) {
+        if (h == 0) p.carry[(base + c0 + k) * 32 + j] = x;
+        float a[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 q = *reinterpret_cast<const f32x4*>(&s_p[buf][k][j * kDenseCarryRow + 8 * g + 4 * h]);
+          a[4 * g] = q.x;
+          a[4 * g + 1] = q.y;
+          a[4 * g + 2] = q.z;
+          a[4 * g + 3] = q.w;
+        }
+        x = dense_matvec(a, xl, h, s_v[buf][k][j]);
+        dense_share(xl, j, h, x);
       }
     }
+    // the other buffer was last read by the chain of block blk - 1, which
+    // the barrier below (of that iteration) has ended
+    if (blk + 1 < nblk) commit(buf ^ 1);
+    __syncthreads();
   }
 }
 
 // one wave per chunk: the carries into its segments, from the chunk's carry
-// and the segment transfers in order
+// and the segment transfers in order. All the transfers the chain needs are
+// read at once: the chain waits for one memory latency, not one per segment.
 __global__ void __launch_bounds__(64) dense_segcarry_kernel(const DenseArgs p) {
   __shared__ __align__(16) float xl[32];
   const int lane = threadIdx.x, j = lane & 31, h = lane >> 5;
   const long long cb = blockIdx.x;  // b * nchunks + c
   float x = p.carry[cb * 32 + j];
-  if (h == 0) xl[j] = x;
-  float a[16], vi;
-  auto load = [&](int w, float (&aa)[16], float& vv) {
+  dense_share(xl, j, h, x);
+  float a[kDenseWaves - 1][16], vi[kDenseWaves - 1];
+#pragma unroll
+  for (int w = 0; w < kDenseWaves - 1; ++w) {
     const float* P = p.Pseg + (cb * kDenseWaves + w) * 1024 + j * 32;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const f32x4 q = *reinterpret_cast<const f32x4*>(P + 8 * g + 4 * h);
-      aa[4 * g] = q.x;
-      aa[4 * g + 1] = q.y;
-      aa[4 * g + 2] = q.z;
-      aa[4 * g + 3] = q.w;
+      a[w][4 * g] = q.x;
+      a[w][4 * g + 1] = q.y;
+      a[w][4 * g + 2] = q.z;
+      a[w][4 * g + 3] = q.w;
     }
-    vv = p.vseg[(cb * kDenseWaves + w) * 32 + j];
-  };
-  load(0, a, vi);
+    vi[w] = p.vseg[(cb * kDenseWaves + w) * 32 + j];
+  }
 #pragma unroll
   for (int w = 0; w < kDenseWaves; ++w) {
-    float an[16], vn = 0.0f;
-    if (w + 1 < kDenseWaves - 1) load(w + 1, an, vn);
     if (h == 0) p.cseg[(cb * kDenseWaves + w) * 32 + j] = x;
     if (w + 1 < kDenseWaves) {
-      x = dense_matvec(a, xl, h, vi);
-      if (h == 0) xl[j] = x;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) a[r] = an[r];
-      vi = vn;
+      x = dense_matvec(a[w], xl, h, vi[w]);
+      dense_share(xl, j, h, x);
     }
   }
 }
@@ -275,7 +326,7 @@ __global__ void __launch_bounds__(64) dense_apply_kernel(const DenseArgs p) {
   const int l_begin = cw * kDenseSeg, l_end = min(l_begin + kDenseSeg, p.L);
   if (l_begin >= p.L) return;  // segment past the end of the sequence (uniform per wave)
   float x = p.cseg[sg * 32 + j];
-  if (h == 0) xl[j] = x;
+  dense_share(xl, j, h, x);
   float a[2][kDenseGroup][16], bs[2][kDenseGroup];
   auto load_group = [&](int g0, float (&ag)[kDenseGroup][16], float (&bg)[kDenseGroup]) {
 #pragma unroll
@@ -296,10 +347,8 @@ __global__ void __launch_bounds__(64) dense_apply_kernel(const DenseArgs p) {
         const int l = gs + t;
         if (l < l_end) {
           x = dense_matvec(a[half][t], xl, h, bs[half][t]);
-          if (h == 0) {
-            xl[j] = x;
-            if (j < p.n) p.s[(row0 + l) * p.n + j] = x;
-          }
+          dense_share(xl, j, h, x);
+          if (h == 0 && j < p.n) p.s[(row0 + l) * p.n + j] = x;
         }
       }
     }
