@@ -13,11 +13,13 @@ from tests.helpers import STATE_TOL, assert_close, say
 
 pytestmark = pytest.mark.gpu
 
-# n = 1, odd and padded sizes, the full 32; L below, at and past one chunk
-# (64 steps) and one segment (8), many chunks, ragged tails
+# n = 1, odd and padded sizes, the full 32; L below, at and past one segment
+# (16 steps) and one chunk (128), many chunks; the chunk carries stage 16
+# chunks at a time: exactly one block (2048 steps), one past it, and 33
+# chunks (a last block of one); ragged tails
 SHAPES = [
     (1, 1, 1), (2, 3, 5), (1, 7, 32), (1, 63, 32), (3, 64, 17), (1, 65, 32), (2, 1000, 32),
-    (2, 777, 8), (1, 4097, 31), (4, 300, 16), (1, 129, 2),
+    (2, 777, 8), (1, 4097, 31), (4, 300, 16), (1, 129, 2), (1, 2048, 32), (2, 2049, 20),
 ]
 
 
