@@ -30,7 +30,11 @@
 //     waves' aggregates, so one barrier per iteration is enough; the last wave
 //     publishes the chunk's inclusive carry;
 //   - per-wave maxima of |d| leave through a cross-lane (DPP) reduction, one
-//     word per wave, reduced over the grid by the finalize launch.
+//     word per wave, reduced over the grid by the finalize launch;
+//   - no descriptor read is left in flight past a branch (loads and stores
+//     share one counter on this GPU: a read the compiler cannot count on
+//     every path turns the next reuse of its registers into a wait for all
+//     memory operations, the previous iteration's stores included).
 //
 // UMODE: where the gate inputs live between iterations. 0: streamed from
 // memory again in every iteration; 1: kept in registers (one HBM read per
