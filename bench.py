@@ -462,8 +462,8 @@ def main(argv=None):
         print(json.dumps(d))
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; the multi-GPU sharding is a design "
-                                   "note, not an implementation", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "the library runs on one GPU; sharding across GPUs is described in the "
+                                   "design notes, not implemented", "n_gpus": args.gpus}))
         return 2
 
     if name in SCAN_WORKLOADS:
@@ -575,7 +575,7 @@ def main(argv=None):
             "algorithmic_slots_per_launch": slots,
             "launch_ms": t_fused,
         },
-        # the same solve in the method's per-iteration form: SURVEY's algorithmic
+        # the same solve in the method's per-iteration form: its algorithmic
         # bytes (inputs + previous iterate read, new iterate written, per iteration)
         "hbm_equivalent": {
             "achieved": sum(bytes_k) / (fused["ms_step"] * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
