@@ -52,19 +52,22 @@ def check_chain(ev, n):
     return steps
 
 
-@pytest.mark.parametrize("schedule", ["fused", "per_iteration"])
+@pytest.mark.parametrize("schedule,early_exit", [("fused", False), ("per_iteration", False),
+                                                 ("per_iteration", True)])
 @pytest.mark.parametrize("cell", ["gru", "lstm"])
-def test_solve_events(cell, schedule):
-    say(f"events solve {cell} {schedule}")
+def test_solve_events(cell, schedule, early_exit):
+    """Early exit runs a row-maximum kernel between the stamped launches."""
+    say(f"events solve {cell} {schedule} early_exit={early_exit}")
     dev = torch.device("cuda:0")
     x = make_inputs(cell, 2, 4096, 256, seed=77, u_dtype="bf16")
     u, a = x.u.to(dev), x.a.to(dev)
     K = 3
     ev = Events(K + 2)
     try:
-        r = binding.solve(cell, u, a, iters=K, schedule=schedule)
+        r = binding.solve(cell, u, a, iters=K, schedule=schedule, early_exit=early_exit)
         ref = r["h"].clone()
-        r2 = binding.solve(cell, u, a, iters=K, schedule=schedule, ws=r["ws"], events=ev.ev)
+        r2 = binding.solve(cell, u, a, iters=K, schedule=schedule, early_exit=early_exit, ws=r["ws"],
+                           events=ev.ev)
         torch.cuda.synchronize()
         assert float((r2["h"] - ref).abs().max()) <= RERUN_TOL
         steps = check_chain(ev, K + 2)
