@@ -55,7 +55,7 @@ struct FusedArgs {
   const float* s0[2];        // initial state per component [B][D]; nullptr = 0
   float* sout[2];            // iterate K per component [B][L][D]
   unsigned long long* incl;  // [K][nchunks][NS][slots]
-  unsigned long long* agg;   // [K][nchunks][NS*NS+NS][slots]
+  unsigned long long* agg;   // [K][nchunks][NS*NS+NS][slots] (look-back mode only)
   unsigned int* ctr;         // [0] ticket
   unsigned int* pmax;        // [K][B][nchunks][ntiles_d][W] per-wave max |update| bits
   int B, L, D, K, nchunks, ntiles_d;
@@ -74,7 +74,7 @@ __device__ __forceinline__ uint32_t wave_max_bits(uint32_t v) {
   return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
 }
 
-template <class Cell, class UT, int C, int T, int W, int LL, int OCC, int UMODE>
+template <class Cell, class UT, int C, int T, int W, int LL, int OCC, int UMODE, bool INCL>
 __global__ void __launch_bounds__(64 * W, OCC) newton_fused_kernel(const FusedArgs p) {
   constexpr int NS = Cell::NS, G = Cell::G;
   constexpr int LD = 64 / LL, CW = LD * C, CL = W * LL * T, NA = NS * NS + NS;
@@ -197,7 +197,7 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_fused_kernel(const FusedAr
     const uint32_t tag = static_cast<uint32_t>(k);
     const int buf = k & 1;
     unsigned long long* incl = p.incl + (k - 1) * inc_k;
-    unsigned long long* agg = p.agg + (k - 1) * agg_k;
+    [[maybe_unused]] unsigned long long* agg = p.agg + (k - 1) * agg_k;
     unsigned long long early[NS][C];  // the predecessor's inclusive carry, read early
     float Jt[T][NS][NS][C], rt[T][NS][C];
     Aff<NS, C> acc;
@@ -316,6 +316,8 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_fused_kernel(const FusedAr
         for (int s = 0; s < NS; ++s)
 #pragma unroll
           for (int c = 0; c < C; ++c) x[s][c] = desc_val(early[s][c]);
+      } else if constexpr (INCL) {
+        wait_incl<NS, C>(incl, BD, chan, LD, chunk - 1, tag, x);
       } else {
         if (wave == W - 1 && ll == 0 && chunk < p.nchunks - 1) {
           Aff<NS, C> tot = wave_agg(0);

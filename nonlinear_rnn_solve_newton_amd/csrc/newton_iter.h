@@ -119,6 +119,32 @@ __device__ __forceinline__ void lookback(unsigned long long* incl, unsigned long
   }
 }
 
+// Waits for chunk i's inclusive carry itself (no composition of aggregates)
+// and returns it. Every word read is tested, so none is left in flight.
+template <int NS, int C>
+__device__ __forceinline__ void wait_incl(unsigned long long* incl, long long BD, long long chan, int cs, int i,
+                                          uint32_t tag, float (&carry)[NS][C]) {
+  while (true) {
+    unsigned long long wi[NS][C];
+    bool ok = true;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        wi[s][c] = desc_get(incl + ((long long)i * NS + s) * BD + chan + c * cs);
+        ok = ok & desc_ok(wi[s][c], tag);
+      }
+    if (ok) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int c = 0; c < C; ++c) carry[s][c] = desc_val(wi[s][c]);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
 template <int NS, int C>
 __device__ __forceinline__ void publish_agg(unsigned long long* agg, long long BD, long long chan, int cs,
                                             int chunk, uint32_t tag, const Aff<NS, C>& e) {
