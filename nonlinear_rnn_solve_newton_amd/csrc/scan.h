@@ -28,7 +28,10 @@ struct ScanArgs {
   int B, L, D, nchunks, ntiles_d;
 };
 
-template <int NS, int C, int T, int W, int LL, int OCC>
+// INCL: the carry into a chunk is the predecessor's inclusive carry, waited
+// for (no aggregates published or composed); chosen by the host where a chunk
+// row has many tiles, so that predecessors run well ahead
+template <int NS, int C, int T, int W, int LL, int OCC, bool INCL>
 __global__ void __launch_bounds__(64 * W, OCC) scan_kernel(const ScanArgs p) {
   constexpr int LD = 64 / LL, CW = LD * C, CL = W * LL * T, NA = NS * NS + NS;
   constexpr uint32_t tag = 1u;
@@ -136,8 +139,12 @@ __global__ void __launch_bounds__(64 * W, OCC) scan_kernel(const ScanArgs p) {
         tot = e;
       }
       if (chunk > 0) {
-        if (chunk < p.nchunks - 1) publish_agg<NS, C>(p.agg, BD, chan, LD, chunk, tag, tot);
-        lookback<NS, C>(p.incl, p.agg, BD, chan, LD, chunk, -1, p.nchunks, tag, carry);
+        if constexpr (INCL) {
+          wait_incl<NS, C>(p.incl, BD, chan, LD, chunk - 1, tag, carry);
+        } else {
+          if (chunk < p.nchunks - 1) publish_agg<NS, C>(p.agg, BD, chan, LD, chunk, tag, tot);
+          lookback<NS, C>(p.incl, p.agg, BD, chan, LD, chunk, -1, p.nchunks, tag, carry);
+        }
       }
       if (chunk < p.nchunks - 1) {
         float x[NS][C];
