@@ -35,7 +35,10 @@ struct AdjArgs {
   int B, L, D, nchunks, ntiles_d;
 };
 
-template <class Cell, class UT, int C, int T, int W, int LL, int OCC>
+// INCL: the chunk carry is the successor chunk's inclusive carry, waited for
+// (no aggregates published or composed); chosen by the host where a chunk row
+// has many tiles, so that the chunks ahead in scan order run well ahead.
+template <class Cell, class UT, int C, int T, int W, int LL, int OCC, bool INCL>
 __global__ void __launch_bounds__(64 * W, OCC) adjoint_kernel(const AdjArgs p) {
   constexpr int NS = Cell::NS, G = Cell::G;
   constexpr int LD = 64 / LL, CW = LD * C, CL = W * LL * T, NA = NS * NS + NS, NSEG = W * LL;
@@ -226,8 +229,12 @@ __global__ void __launch_bounds__(64 * W, OCC) adjoint_kernel(const AdjArgs p) {
         tot = e;
       }
       if (chunk < p.nchunks - 1) {
-        if (chunk > 0) publish_agg<NS, C>(p.agg, BD, chan, LD, chunk, tag, tot);
-        lookback<NS, C>(p.incl, p.agg, BD, chan, LD, chunk, +1, p.nchunks, tag, carry);
+        if constexpr (INCL) {
+          wait_incl<NS, C>(p.incl, BD, chan, LD, chunk + 1, tag, carry);
+        } else {
+          if (chunk > 0) publish_agg<NS, C>(p.agg, BD, chan, LD, chunk, tag, tot);
+          lookback<NS, C>(p.incl, p.agg, BD, chan, LD, chunk, +1, p.nchunks, tag, carry);
+        }
       }
       if (chunk > 0) {
         float x[NS][C];

@@ -171,7 +171,10 @@ __device__ __forceinline__ void publish_incl(unsigned long long* incl, long long
 
 // FIRST: the launch of iteration 1, whose previous iterate is zero at every
 // step (no state input); only the initial state s0 enters, at l = 0.
-template <class Cell, class UT, int C, int T, int W, int LL, int OCC, bool FIRST>
+// INCL: the chunk carry is the predecessor's inclusive carry, waited for (no
+// aggregates published or composed); chosen by the host where a chunk row
+// has many tiles, so that predecessors run well ahead.
+template <class Cell, class UT, int C, int T, int W, int LL, int OCC, bool FIRST, bool INCL>
 __global__ void __launch_bounds__(64 * W, OCC) newton_iter_kernel(const IterArgs p) {
   constexpr int NS = Cell::NS, G = Cell::G;
   constexpr int LD = 64 / LL;   // lanes along D
@@ -370,8 +373,12 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_iter_kernel(const IterArgs
         tot = e;
       }
       if (chunk > 0) {
-        if (chunk < p.nchunks - 1) publish_agg<NS, C>(p.agg, BD, chan, LD, chunk, tag, tot);
-        lookback<NS, C>(p.incl, p.agg, BD, chan, LD, chunk, -1, p.nchunks, tag, carry);
+        if constexpr (INCL) {
+          wait_incl<NS, C>(p.incl, BD, chan, LD, chunk - 1, tag, carry);
+        } else {
+          if (chunk < p.nchunks - 1) publish_agg<NS, C>(p.agg, BD, chan, LD, chunk, tag, tot);
+          lookback<NS, C>(p.incl, p.agg, BD, chan, LD, chunk, -1, p.nchunks, tag, carry);
+        }
       }
       if (chunk < p.nchunks - 1) {
         float x[NS][C];

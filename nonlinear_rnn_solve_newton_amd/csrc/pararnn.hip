@@ -269,7 +269,7 @@ int clear_ws(char* ws, const Layout& y, float* user, long long nuser, hipStream_
   return check_hip(hipGetLastError());
 }
 
-template <class Cell, class UT, int C>
+template <class Cell, class UT, int C, bool INCL>
 int launch_iter(const IterArgs& a, hipStream_t s, Stamps t) {
   using K = Cfg<Cell, C, false>;
   using K1 = CfgFirst<Cell, C>;
@@ -278,51 +278,65 @@ int launch_iter(const IterArgs& a, hipStream_t s, Stamps t) {
   const unsigned grid = static_cast<unsigned>(a.B) * a.ntiles_d * static_cast<unsigned>(a.nchunks);
   const IterArgs& b = a;
   if (a.k == 1)  // iteration 1 starts from the zero iterate and reads no state
-    return launch(newton_iter_kernel<Cell, UT, C, K1::T, K1::W, K1::LL, K1::OCC, true>, dim3(grid),
+    return launch(newton_iter_kernel<Cell, UT, C, K1::T, K1::W, K1::LL, K1::OCC, true, INCL>, dim3(grid),
                   dim3(64 * K1::W), s, t, b);
-  return launch(newton_iter_kernel<Cell, UT, C, K::T, K::W, K::LL, K::OCC, false>, dim3(grid), dim3(64 * K::W),
-                s, t, b);
+  return launch(newton_iter_kernel<Cell, UT, C, K::T, K::W, K::LL, K::OCC, false, INCL>, dim3(grid),
+                dim3(64 * K::W), s, t, b);
 }
 
 template <class Cell, class UT>
-int launch_iter_c(int C, const IterArgs& a, hipStream_t s, Stamps t) {
+int launch_iter_c(int C, bool incl, const IterArgs& a, hipStream_t s, Stamps t) {
   if constexpr (max_c<Cell, false>() >= 4) {
-    if (C == 4) return launch_iter<Cell, UT, 4>(a, s, t);
+    if (C == 4) return incl ? launch_iter<Cell, UT, 4, true>(a, s, t) : launch_iter<Cell, UT, 4, false>(a, s, t);
   }
   if constexpr (max_c<Cell, false>() >= 2) {
-    if (C == 2) return launch_iter<Cell, UT, 2>(a, s, t);
+    if (C == 2) return incl ? launch_iter<Cell, UT, 2, true>(a, s, t) : launch_iter<Cell, UT, 2, false>(a, s, t);
   }
-  return launch_iter<Cell, UT, 1>(a, s, t);
+  return incl ? launch_iter<Cell, UT, 1, true>(a, s, t) : launch_iter<Cell, UT, 1, false>(a, s, t);
 }
 
 template <class Cell>
-int launch_iter_any(int dtype, int C, const IterArgs& a, hipStream_t s, Stamps t) {
-  return dtype == PARARNN_BF16 ? launch_iter_c<Cell, bf16>(C, a, s, t) : launch_iter_c<Cell, float>(C, a, s, t);
+int launch_iter_any(int dtype, int C, bool incl, const IterArgs& a, hipStream_t s, Stamps t) {
+  return dtype == PARARNN_BF16 ? launch_iter_c<Cell, bf16>(C, incl, a, s, t)
+                               : launch_iter_c<Cell, float>(C, incl, a, s, t);
 }
 
-template <class Cell, class UT, int C>
+template <class Cell, class UT, int C, bool INCL>
 int launch_adj(const AdjArgs& a, hipStream_t s, Stamps t) {
   using K = Cfg<Cell, C, true>;
   const unsigned grid = static_cast<unsigned>(a.B) * a.ntiles_d * static_cast<unsigned>(a.nchunks);
   const AdjArgs& b = a;
-  return launch(adjoint_kernel<Cell, UT, C, K::T, K::W, K::LL, K::OCC>, dim3(grid), dim3(64 * K::W), s, t, b);
+  return launch(adjoint_kernel<Cell, UT, C, K::T, K::W, K::LL, K::OCC, INCL>, dim3(grid), dim3(64 * K::W), s, t,
+                b);
 }
 
 template <class Cell, class UT>
-int launch_adj_c(int C, const AdjArgs& a, hipStream_t s, Stamps t) {
+int launch_adj_c(int C, bool incl, const AdjArgs& a, hipStream_t s, Stamps t) {
   if constexpr (max_c<Cell, true>() >= 4) {
-    if (C == 4) return launch_adj<Cell, UT, 4>(a, s, t);
+    if (C == 4) return incl ? launch_adj<Cell, UT, 4, true>(a, s, t) : launch_adj<Cell, UT, 4, false>(a, s, t);
   }
   if constexpr (max_c<Cell, true>() >= 2) {
-    if (C == 2) return launch_adj<Cell, UT, 2>(a, s, t);
+    if (C == 2) return incl ? launch_adj<Cell, UT, 2, true>(a, s, t) : launch_adj<Cell, UT, 2, false>(a, s, t);
   }
-  return launch_adj<Cell, UT, 1>(a, s, t);
+  return incl ? launch_adj<Cell, UT, 1, true>(a, s, t) : launch_adj<Cell, UT, 1, false>(a, s, t);
 }
 
 template <class Cell>
-int launch_adj_any(int dtype, int C, const AdjArgs& a, hipStream_t s, Stamps t) {
-  return dtype == PARARNN_BF16 ? launch_adj_c<Cell, bf16>(C, a, s, t) : launch_adj_c<Cell, float>(C, a, s, t);
+int launch_adj_any(int dtype, int C, bool incl, const AdjArgs& a, hipStream_t s, Stamps t) {
+  return dtype == PARARNN_BF16 ? launch_adj_c<Cell, bf16>(C, incl, a, s, t)
+                               : launch_adj_c<Cell, float>(C, incl, a, s, t);
 }
+
+// The per-iteration Newton kernel's and the adjoint's chunk carry from the
+// neighbouring chunk's inclusive carry alone where a chunk row has at least
+// this many tiles (see kInclOnlyTiles for the fused kernel). Same-box
+// measurements, inclusive only against look-back:
+//   tiles per row              16      32      64      128 and more
+//   per-iteration solve, GRU   +88%    +31%    +4%     -3%
+//   per-iteration solve, LSTM                  -4.5%   -5%
+//   adjoint, GRU               +80%    +25%    0%      -4%
+//   adjoint, LSTM              +49%    +13%    -6%     -5.5%
+long long iter_incl_tiles(int cell) { return cell == PARARNN_LSTM ? 64 : 128; }
 
 template <int NS, int C>
 int launch_scan(bool incl, const ScanArgs& a, hipStream_t s, Stamps t) {
@@ -503,7 +517,10 @@ int solve(int cell, const void* u, const float* a, const float* c0, const float*
 
   int rc = record(o, 0, stream);
   if (rc) return rc;
-  rc = clear_ws(w, y, nullptr, 0, stream);
+  const bool incl_only = static_cast<long long>(o->B) * y.ntiles_d >= iter_incl_tiles(cell);
+  Layout yc = y;  // inclusive only: the aggregate descriptors are never read
+  if (incl_only) yc.zero_end = y.agg;
+  rc = clear_ws(w, yc, nullptr, 0, stream);
   if (rc) return rc;
 
   IterArgs ia;
@@ -535,8 +552,8 @@ int solve(int cell, const void* u, const float* a, const float* c0, const float*
     ia.k = k;
     // launch k stamps event k + 1 at its end (and launch 1 event 1 at its start)
     const Stamps t = stamps(o, k == 1 ? 1 : -1, k + 1);
-    rc = (cell == PARARNN_LSTM) ? launch_iter_any<LstmCell>(o->u_dtype, C, ia, stream, t)
-                                : launch_iter_any<GruCell>(o->u_dtype, C, ia, stream, t);
+    rc = (cell == PARARNN_LSTM) ? launch_iter_any<LstmCell>(o->u_dtype, C, incl_only, ia, stream, t)
+                                : launch_iter_any<GruCell>(o->u_dtype, C, incl_only, ia, stream, t);
     if (rc) return rc;
     if (o->early_exit) {  // the next launch decides from this launch's row maxima
       hipLaunchKernelGGL(rowmax_kernel, dim3(o->B), dim3(kRowmaxThreads), 0, stream, ia.pmax, ia.maxupd, o->B, y.ntiles_d,
@@ -690,7 +707,10 @@ extern "C" int32_t pararnn_adjoint(int32_t cell, const void* u, const float* a, 
 
   int rc = record(o, 0, stream);
   if (rc) return rc;
-  rc = clear_ws(w, y, nullptr, 0, stream);
+  const bool incl_only = static_cast<long long>(o->B) * y.ntiles_d >= iter_incl_tiles(cell);
+  Layout yc = y;  // inclusive only: the aggregate descriptors are never read
+  if (incl_only) yc.zero_end = y.agg;
+  rc = clear_ws(w, yc, nullptr, 0, stream);
   if (rc) return rc;
 
   AdjArgs aa;
@@ -715,8 +735,8 @@ extern "C" int32_t pararnn_adjoint(int32_t cell, const void* u, const float* a, 
   aa.ntiles_d = y.ntiles_d;
   // the adjoint launch stamps event 1 at its start; event 2 at the end of
   // the last launch (the da reduction when requested)
-  rc = lstm ? launch_adj_any<LstmCell>(o->u_dtype, C, aa, stream, stamps(o, 1, da ? -1 : 2))
-            : launch_adj_any<GruCell>(o->u_dtype, C, aa, stream, stamps(o, 1, da ? -1 : 2));
+  rc = lstm ? launch_adj_any<LstmCell>(o->u_dtype, C, incl_only, aa, stream, stamps(o, 1, da ? -1 : 2))
+            : launch_adj_any<GruCell>(o->u_dtype, C, incl_only, aa, stream, stamps(o, 1, da ? -1 : 2));
   if (rc) return rc;
   if (da) {
     const int G = ngates(cell);
