@@ -86,16 +86,26 @@ __device__ __forceinline__ void dense_load_row(const DenseArgs& p, long long ste
   }
 }
 
-// Lanes (i, 0) publish element i of the wave's vector in its LDS slot xl for
-// the next dense_matvec. The LDS operations of one wave complete in order, so
-// the exchange needs no workgroup barrier; the fences and the wave barrier
-// tell the compiler that other lanes wrote the slot. Without them a lane that
-// wrote nothing may keep what it read before, or read before the write.
+// Lanes (i, 0) and (i, 1), which hold the same value, publish element i of
+// the wave's vector in its LDS slot xl for the next dense_matvec (both write,
+// so no lane mask splits the code around the store). The LDS operations of
+// one wave complete in order, so the exchange needs no workgroup barrier; the
+// fences and the wave barrier tell the compiler that other lanes wrote the
+// slot. Without them a lane may keep what it read before, or read before the
+// write.
 __device__ __forceinline__ void dense_share(float* xl, int i, int h, float x) {
-  if (h == 0) xl[i] = x;
+  (void)h;
+  xl[i] = x;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// part[lane] + part[lane ^ 32]: one swap of the two half-waves' values
+// between registers (gfx950), no LDS round trip
+__device__ __forceinline__ float dense_halves_sum(float part) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
 // y[i] = sum_q a[i][q] x[q] + bi in lanes i and i + 32, with x[q] read from
@@ -111,7 +121,7 @@ __device__ __forceinline__ float dense_matvec(const float (&a)[16], const float*
     pg[g] = fmaf(a[4 * g + 3], xv.w, pg[g]);
   }
   const float part = (pg[0] + pg[1]) + (pg[2] + pg[3]);
-  return part + __shfl_xor(part, 32, 64) + bi;
+  return dense_halves_sum(part) + bi;
 }
 
 // Q <- A Q with A given as row values a (this lane's row, columns R(r, h))
@@ -141,22 +151,34 @@ __global__ void __launch_bounds__(64 * kDenseWaves) dense_chunk_kernel(const Den
   for (int r = 0; r < 16; ++r) Q[r] = (dense_row(r, h) == j) ? 1.0f : 0.0f;
   float v = 0.0f;
   dense_share(xl, j, h, 0.0f);
-  // rows stream through a ring of kDenseRing steps ahead of the chain
+  // rows stream through a ring of kDenseRing steps ahead of the chain. The
+  // loads are unconditional, their step clamped into the row (steps past the
+  // end are read and not used): a load behind a branch leaves the compiler
+  // unable to count the loads in flight, and it then waits for all of them
+  // before each step, which empties the ring.
+  const int l_last = p.L - 1;
   float a[kDenseRing][16], bs[kDenseRing];
 #pragma unroll
-  for (int t = 0; t < kDenseRing; ++t) {
-    if (l_begin + t < l_end) dense_load_row<N32>(p, row0 + l_begin + t, j, h, a[t], bs[t]);
-  }
+  for (int t = 0; t < kDenseRing; ++t)
+    dense_load_row<N32>(p, row0 + min(l_begin + t, l_last), j, h, a[t], bs[t]);
+  // Steps past the end of the sequence act as the identity (A = I, b = 0),
+  // selected rather than branched around: each step is straight code, in
+  // which the compiler can overlap the vector chain v with the independent
+  // matrix-core chain Q. A scheduling barrier closes each step, so that its
+  // prefetch load is not moved down to where the row is used.
 #pragma unroll
   for (int t = 0; t < kDenseSeg; ++t) {
-    if (l_begin + t < l_end) {
-      const int k = t % kDenseRing;
-      v = dense_matvec(a[k], xl, h, bs[k]);
-      dense_share(xl, j, h, v);
-      Q = dense_mfma_chain(a[k], Q);
-      if (t + kDenseRing < kDenseSeg && l_begin + t + kDenseRing < l_end)
-        dense_load_row<N32>(p, row0 + l_begin + t + kDenseRing, j, h, a[k], bs[k]);
-    }
+    const int k = t % kDenseRing;
+    const bool live = l_begin + t < l_end;
+    float ak[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ak[r] = live ? a[k][r] : (dense_row(r, h) == j ? 1.0f : 0.0f);
+    v = dense_matvec(ak, xl, h, live ? bs[k] : 0.0f);
+    dense_share(xl, j, h, v);
+    Q = dense_mfma_chain(ak, Q);
+    if (t + kDenseRing < kDenseSeg)
+      dense_load_row<N32>(p, row0 + min(l_begin + t + kDenseRing, l_last), j, h, a[k], bs[k]);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   {  // the segment's own transfer, for the carries into the segments
@@ -311,10 +333,12 @@ __global__ void __launch_bounds__(64) dense_segcarry_kernel(const DenseArgs p) {
   }
 }
 
-// one wave per segment: the recurrence from the segment's carry; the rows of
-// A stream in groups of kDenseGroup steps, the next group in flight while the
-// current one is applied
-constexpr int kDenseGroup = 4;
+// one wave per segment: the recurrence from the segment's carry. The rows of
+// A stream through a ring of kDenseApplyRing steps ahead of the recurrence,
+// loaded unconditionally with the step clamped into the row, so that the
+// compiler counts the loads in flight and each step waits for its own rows
+// only (a load behind a branch makes it wait for all of them).
+constexpr int kDenseApplyRing = 8;
 template <bool N32>
 __global__ void __launch_bounds__(64) dense_apply_kernel(const DenseArgs p) {
   __shared__ __align__(16) float xl[32];
@@ -323,35 +347,24 @@ __global__ void __launch_bounds__(64) dense_apply_kernel(const DenseArgs p) {
   const int b = static_cast<int>(sg / (static_cast<long long>(p.nchunks) * kDenseWaves));
   const int cw = static_cast<int>(sg - static_cast<long long>(b) * p.nchunks * kDenseWaves);  // c * W + w
   const long long row0 = static_cast<long long>(b) * p.L;
-  const int l_begin = cw * kDenseSeg, l_end = min(l_begin + kDenseSeg, p.L);
+  const int l_begin = cw * kDenseSeg, l_end = min(l_begin + kDenseSeg, p.L), l_last = p.L - 1;
   if (l_begin >= p.L) return;  // segment past the end of the sequence (uniform per wave)
   float x = p.cseg[sg * 32 + j];
   dense_share(xl, j, h, x);
-  float a[2][kDenseGroup][16], bs[2][kDenseGroup];
-  auto load_group = [&](int g0, float (&ag)[kDenseGroup][16], float (&bg)[kDenseGroup]) {
+  float a[kDenseApplyRing][16], bs[kDenseApplyRing];
 #pragma unroll
-    for (int t = 0; t < kDenseGroup; ++t) {
-      if (g0 + t < l_end) dense_load_row<N32>(p, row0 + g0 + t, j, h, ag[t], bg[t]);
+  for (int t = 0; t < kDenseApplyRing; ++t)
+    dense_load_row<N32>(p, row0 + min(l_begin + t, l_last), j, h, a[t], bs[t]);
+#pragma unroll
+  for (int t = 0; t < kDenseSeg; ++t) {
+    const int k = t % kDenseApplyRing, l = l_begin + t;
+    if (l < l_end) {
+      x = dense_matvec(a[k], xl, h, bs[k]);
+      dense_share(xl, j, h, x);
+      if (h == 0 && j < p.n) p.s[(row0 + l) * p.n + j] = x;
     }
-  };
-  load_group(l_begin, a[0], bs[0]);
-  for (int g0 = l_begin; g0 < l_end; g0 += 2 * kDenseGroup) {
-    if (g0 + kDenseGroup < l_end) load_group(g0 + kDenseGroup, a[1], bs[1]);
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int gs = g0 + half * kDenseGroup;
-      // the group after next starts loading while the second one is applied
-      if (half == 1 && g0 + 2 * kDenseGroup < l_end) load_group(g0 + 2 * kDenseGroup, a[0], bs[0]);
-#pragma unroll
-      for (int t = 0; t < kDenseGroup; ++t) {
-        const int l = gs + t;
-        if (l < l_end) {
-          x = dense_matvec(a[half][t], xl, h, bs[half][t]);
-          dense_share(xl, j, h, x);
-          if (h == 0 && j < p.n) p.s[(row0 + l) * p.n + j] = x;
-        }
-      }
-    }
+    if (t + kDenseApplyRing < kDenseSeg)
+      dense_load_row<N32>(p, row0 + min(l + kDenseApplyRing, l_last), j, h, a[k], bs[k]);
   }
 }
 
