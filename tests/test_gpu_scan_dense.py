@@ -58,8 +58,8 @@ def test_scan_dense_rejects_large_state():
 
 @pytest.mark.parametrize("name", list(DENSE_WORKLOADS))
 def test_scan_dense_workload(name):
-    """The full-size dense workload in the benchmark's launch configuration:
-    16 sampled batch-row prefixes against the oracle."""
+    """The full-size dense workload in the benchmark's launch configuration,
+    every output against the oracle's loop (one fp64 pass per batch row)."""
     w = DENSE_WORKLOADS[name]
     say(f"dense workload {name}")
     x = dense_workload_inputs(w)
