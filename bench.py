@@ -284,7 +284,7 @@ def bench_scan_dense(w, args):
         "vs_baseline": None, "dtype": "f32",
         "data": "synthetic (seeded; A = 0.95 x random orthogonal, b, s0 ~ N(0,1))",
         "config": {"workload": w.name, "B": w.B, "L": w.L, "n": w.n},
-        "roofline": {"bound": "hbm", "kernel": "dense_chunk_kernel + dense_carry_kernel + dense_segcarry_kernel + dense_apply_kernel",
+        "roofline": {"bound": "hbm", "kernel": "dense_chunk_kernel + dense_carry_kernel + dense_apply_kernel",
                      "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                      "traffic": load_traffic(w.name, source_digest(), "dense"),
                      "algorithmic_bytes_per_launch": [nbytes], "launch_ms": [t]},

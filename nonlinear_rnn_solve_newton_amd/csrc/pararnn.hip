@@ -572,7 +572,7 @@ int solve(int cell, const void* u, const float* a, const float* c0, const float*
 // and carries [B][nchunks][32] each (nothing to clear: every entry is written
 // before it is read)
 struct DenseLayout {
-  size_t P = 0, v = 0, carry = 0, Pseg = 0, vseg = 0, cseg = 0, total = 0;
+  size_t P = 0, v = 0, carry = 0, Pseg = 0, vseg = 0, total = 0;
   int nchunks = 0;
 };
 
@@ -585,8 +585,7 @@ DenseLayout dense_layout(const pararnn_opts* o) {
   y.carry = round_up(y.v + sizeof(float) * nc * 32);
   y.Pseg = round_up(y.carry + sizeof(float) * nc * 32);
   y.vseg = round_up(y.Pseg + sizeof(float) * ns * 1024);
-  y.cseg = round_up(y.vseg + sizeof(float) * ns * 32);
-  y.total = round_up(y.cseg + sizeof(float) * ns * 32);
+  y.total = round_up(y.vseg + sizeof(float) * ns * 32);
   return y;
 }
 
@@ -611,7 +610,6 @@ int scan_dense(const float* A, const float* b, const float* s0, float* s, void* 
   da.carry = reinterpret_cast<float*>(w + y.carry);
   da.Pseg = reinterpret_cast<float*>(w + y.Pseg);
   da.vseg = reinterpret_cast<float*>(w + y.vseg);
-  da.cseg = reinterpret_cast<float*>(w + y.cseg);
   da.B = o->B;
   da.L = o->L;
   da.n = o->D;
@@ -626,9 +624,6 @@ int scan_dense(const float* A, const float* b, const float* s0, float* s, void* 
            : launch(dense_chunk_kernel<false>, dim3(nwg), dim3(64 * kDenseWaves), stream, stamps(o, 1, -1), da);
   if (rc) return rc;
   hipLaunchKernelGGL(dense_carry_kernel, dim3(static_cast<unsigned>(o->B)), dim3(64 * kDenseCarryWaves), 0, stream, da);
-  rc = check_hip(hipGetLastError());
-  if (rc) return rc;
-  hipLaunchKernelGGL(dense_segcarry_kernel, dim3(nwg), dim3(64), 0, stream, da);
   rc = check_hip(hipGetLastError());
   if (rc) return rc;
   const unsigned nseg = nwg * kDenseWaves;

@@ -5,15 +5,17 @@
 // n^2 and the products as n^3, which is why the diagonal cells exist; for
 // small n it is still a few GEMM-shaped products per step).
 //
-// Four launches over chunks of kDenseChunk steps of one batch row:
+// Three launches over chunks of kDenseChunk steps of one batch row:
 //   1. dense_chunk_kernel: the transfer P = A_end ... A_start (a chain of
 //      32 x 32 x 32 products on the matrix cores, fp32) and local solution v
-//      from zero of every segment of kDenseSeg steps (one wave each), and of
-//      the chunk, the segments combined by a tree through LDS;
+//      from zero of every segment of kDenseSeg steps (one wave each), then an
+//      inclusive scan of these over the chunk's segments through LDS: the
+//      chunk's transfer, and for every segment the transfer and local
+//      solution of the segments before it;
 //   2. dense_carry_kernel: per batch row, the carries into the chunks,
 //      x_{c+1} = P_c x_c + v_c from s0, one matrix-vector product per chunk;
-//   3. dense_segcarry_kernel: per chunk, the carries into its segments;
-//   4. dense_apply_kernel: per segment, the recurrence itself from its carry,
+//   3. dense_apply_kernel: per segment, its carry from the chunk's (one
+//      matrix-vector product with the prefix), then the recurrence itself,
 //      one matrix-vector product per step, writing s.
 // Everything runs in a 32 x 32 frame: entries past n are zero, and so stay
 // the padded state components.
@@ -48,9 +50,8 @@ struct DenseArgs {
   float* P;         // [B][nchunks][32][32] chunk transfers (workspace)
   float* v;         // [B][nchunks][32] chunk local solutions (workspace)
   float* carry;     // [B][nchunks][32] carries into the chunks (workspace)
-  float* Pseg;      // [B][nchunks][kDenseWaves][32][32] segment transfers (workspace)
-  float* vseg;      // [B][nchunks][kDenseWaves][32] segment local solutions (workspace)
-  float* cseg;      // [B][nchunks][kDenseWaves][32] carries into the segments (workspace)
+  float* Pseg;      // [B][nchunks][kDenseWaves][32][32] transfers of the segments before each (workspace)
+  float* vseg;      // [B][nchunks][kDenseWaves][32] their local solutions (workspace)
   int B, L, n, nchunks;
 };
 
@@ -134,8 +135,8 @@ __device__ __forceinline__ f32x16 dense_mfma_chain(const float (&a)[16], const f
 
 template <bool N32>
 __global__ void __launch_bounds__(64 * kDenseWaves) dense_chunk_kernel(const DenseArgs p) {
-  __shared__ float s_q[kDenseWaves / 2][32][33];  // transfers handed down the tree (padded rows)
-  __shared__ float s_v[kDenseWaves / 2][32];
+  __shared__ float s_q[kDenseWaves][32][33];  // the waves' transfers at each scan level (padded rows)
+  __shared__ __align__(16) float s_v[kDenseWaves][32];
   __shared__ __align__(16) float s_x[kDenseWaves][32];  // each wave's running vector
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 31, h = lane >> 5;
@@ -181,39 +182,43 @@ __global__ void __launch_bounds__(64 * kDenseWaves) dense_chunk_kernel(const Den
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  {  // the segment's own transfer, for the carries into the segments
-    const long long sg = (static_cast<long long>(b) * p.nchunks + c) * kDenseWaves + wave;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) p.Pseg[sg * 1024 + dense_row(r, h) * 32 + j] = Q[r];
-    if (h == 0) p.vseg[sg * 32 + j] = v;
-  }
-
-  // tree over the waves: at distance d, wave w (w % 2d == 0) takes the
-  // segment of wave w + d, which follows it: Q_w <- Q_{w+d} Q_w, v_w <- Q_{w+d} v_w + v_{w+d}
+  // inclusive scan over the chunk's segments (three levels): at distance d,
+  // wave w >= d composes its range with the one that ends at wave w - d and
+  // precedes it, Q_w <- Q_w Q_{w-d}, v_w <- Q_w v_{w-d} + v_w. Wave w's own
+  // transfer is read back in row layout (the products' first operand), the
+  // other's in accumulator layout.
   for (int d = 1; d < kDenseWaves; d *= 2) {
-    const bool giver = (wave % (2 * d)) == d;
-    const int slot = wave / (2 * d);
-    if (giver) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s_q[slot][dense_row(r, h)][j] = Q[r];
-      if (h == 0) s_v[slot][j] = v;
-    }
+    for (int r = 0; r < 16; ++r) s_q[wave][dense_row(r, h)][j] = Q[r];
+    s_v[wave][j] = v;
     __syncthreads();
-    if ((wave % (2 * d)) == 0) {
+    if (wave >= d) {
       float aq[16];
+      f32x16 Qo;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) aq[r] = s_q[slot][j][dense_row(r, h)];
-      v = dense_matvec(aq, xl, h, s_v[slot][j]);
-      if (h == 0) xl[j] = v;
-      Q = dense_mfma_chain(aq, Q);
+      for (int r = 0; r < 16; ++r) {
+        aq[r] = s_q[wave][j][dense_row(r, h)];
+        Qo[r] = s_q[wave - d][dense_row(r, h)][j];
+      }
+      v = dense_matvec(aq, s_v[wave - d], h, v);
+      Q = dense_mfma_chain(aq, Qo);
     }
     __syncthreads();
   }
-  if (wave == 0) {
-    float* P = p.P + (static_cast<long long>(b) * p.nchunks + c) * 1024;
+  // wave w now holds segments 0 .. w composed: the prefix of segment w + 1,
+  // and for the last wave the chunk's transfer; segment 0's prefix is the
+  // identity
+  const long long cbi = static_cast<long long>(b) * p.nchunks + c;
+  const bool last = wave == kDenseWaves - 1;
+  float* Pd = last ? p.P + cbi * 1024 : p.Pseg + (cbi * kDenseWaves + wave + 1) * 1024;
+  float* vd = last ? p.v + cbi * 32 : p.vseg + (cbi * kDenseWaves + wave + 1) * 32;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) P[dense_row(r, h) * 32 + j] = Q[r];
-    if (h == 0) p.v[(static_cast<long long>(b) * p.nchunks + c) * 32 + j] = v;
+  for (int r = 0; r < 16; ++r) Pd[dense_row(r, h) * 32 + j] = Q[r];
+  if (h == 0) vd[j] = v;
+  if (wave == 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p.Pseg[cbi * kDenseWaves * 1024 + dense_row(r, h) * 32 + j] = (dense_row(r, h) == j) ? 1.0f : 0.0f;
+    if (h == 0) p.vseg[cbi * kDenseWaves * 32 + j] = 0.0f;
   }
 }
 
@@ -300,44 +305,15 @@ __global__ void __launch_bounds__(64 * kDenseCarryWaves) dense_carry_kernel(cons
   }
 }
 
-// one wave per chunk: the carries into its segments, from the chunk's carry
-// and the segment transfers in order. All the transfers the chain needs are
-// read at once: the chain waits for one memory latency, not one per segment.
-__global__ void __launch_bounds__(64) dense_segcarry_kernel(const DenseArgs p) {
-  __shared__ __align__(16) float xl[32];
-  const int lane = threadIdx.x, j = lane & 31, h = lane >> 5;
-  const long long cb = blockIdx.x;  // b * nchunks + c
-  float x = p.carry[cb * 32 + j];
-  dense_share(xl, j, h, x);
-  float a[kDenseWaves - 1][16], vi[kDenseWaves - 1];
-#pragma unroll
-  for (int w = 0; w < kDenseWaves - 1; ++w) {
-    const float* P = p.Pseg + (cb * kDenseWaves + w) * 1024 + j * 32;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const f32x4 q = *reinterpret_cast<const f32x4*>(P + 8 * g + 4 * h);
-      a[w][4 * g] = q.x;
-      a[w][4 * g + 1] = q.y;
-      a[w][4 * g + 2] = q.z;
-      a[w][4 * g + 3] = q.w;
-    }
-    vi[w] = p.vseg[(cb * kDenseWaves + w) * 32 + j];
-  }
-#pragma unroll
-  for (int w = 0; w < kDenseWaves; ++w) {
-    if (h == 0) p.cseg[(cb * kDenseWaves + w) * 32 + j] = x;
-    if (w + 1 < kDenseWaves) {
-      x = dense_matvec(a[w], xl, h, vi[w]);
-      dense_share(xl, j, h, x);
-    }
-  }
-}
-
-// one wave per segment: the recurrence from the segment's carry. The rows of
-// A stream through a ring of kDenseApplyRing steps ahead of the recurrence,
-// loaded unconditionally with the step clamped into the row, so that the
-// compiler counts the loads in flight and each step waits for its own rows
-// only (a load behind a branch makes it wait for all of them).
+// one wave per segment: the carry into the segment, x = E x_c + e from the
+// chunk's carry x_c with the transfer E and local solution e of the
+// segments before it, then the recurrence from it. The rows of A stream
+// through a ring of kDenseApplyRing steps ahead of the recurrence, loaded
+// unconditionally with the step clamped into the row, so that the compiler
+// counts the loads in flight and each step waits for its own rows only (a
+// load behind a branch makes it wait for all of them). E, e and x_c are
+// loaded first: the load counter is in order, so waiting for them leaves
+// the ring in flight.
 constexpr int kDenseApplyRing = 8;
 template <bool N32>
 __global__ void __launch_bounds__(64) dense_apply_kernel(const DenseArgs p) {
@@ -349,12 +325,29 @@ __global__ void __launch_bounds__(64) dense_apply_kernel(const DenseArgs p) {
   const long long row0 = static_cast<long long>(b) * p.L;
   const int l_begin = cw * kDenseSeg, l_end = min(l_begin + kDenseSeg, p.L), l_last = p.L - 1;
   if (l_begin >= p.L) return;  // segment past the end of the sequence (uniform per wave)
-  float x = p.cseg[sg * 32 + j];
-  dense_share(xl, j, h, x);
+  float e[16];
+  {
+    const float* E = p.Pseg + sg * 1024 + j * 32;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 q = *reinterpret_cast<const f32x4*>(E + 8 * g + 4 * h);
+      e[4 * g] = q.x;
+      e[4 * g + 1] = q.y;
+      e[4 * g + 2] = q.z;
+      e[4 * g + 3] = q.w;
+    }
+  }
+  const float ev = p.vseg[sg * 32 + j];
+  const float xc = p.carry[(sg / kDenseWaves) * 32 + j];
+  __builtin_amdgcn_sched_barrier(0);
   float a[kDenseApplyRing][16], bs[kDenseApplyRing];
 #pragma unroll
   for (int t = 0; t < kDenseApplyRing; ++t)
     dense_load_row<N32>(p, row0 + min(l_begin + t, l_last), j, h, a[t], bs[t]);
+  __builtin_amdgcn_sched_barrier(0);
+  dense_share(xl, j, h, xc);
+  float x = dense_matvec(e, xl, h, ev);
+  dense_share(xl, j, h, x);
 #pragma unroll
   for (int t = 0; t < kDenseSeg; ++t) {
     const int k = t % kDenseApplyRing, l = l_begin + t;
