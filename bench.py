@@ -135,16 +135,22 @@ def traffic_from_counters(workload: str, fetch_csv: str, write_csv: str, iters: 
         rows.sort(key=lambda r: int(r["Dispatch_Id"]))
         copy = [float(r["Counter_Value"]) * 1024 for r in rows
                 if "copyBuffer" in r["Kernel_Name"] and float(r["Counter_Value"]) > 1e5]
-        tag = "pararnn::dense_" if kernel == "dense" else f"{kernel}_kernel"
-        its = [float(r["Counter_Value"]) * 1024 for r in rows if tag in r["Kernel_Name"]]
+        if kernel == "dense":  # one scan = the launches from one transfer launch to the next
+            its = []
+            for r in rows:
+                if "pararnn::dense_" not in r["Kernel_Name"]:
+                    continue
+                if "dense_chunk_kernel" in r["Kernel_Name"]:
+                    its.append(0.0)
+                if its:
+                    its[-1] += float(r["Counter_Value"]) * 1024
+            return copy, its
+        its = [float(r["Counter_Value"]) * 1024 for r in rows if f"{kernel}_kernel" in r["Kernel_Name"]]
         return copy, its
 
     calib = float(1 << 30)
     fc, fi = read(fetch_csv, "FETCH_SIZE")
     wc, wi = read(write_csv, "WRITE_SIZE")
-    if kernel == "dense":  # four launches per scan: sum each scan's launches
-        fi = [sum(fi[i:i + 4]) for i in range(0, len(fi) - 3, 4)]
-        wi = [sum(wi[i:i + 4]) for i in range(0, len(wi) - 3, 4)]
     fscale = calib / (sum(fc) / len(fc))
     wscale = calib / (sum(wc) / len(wc))
     # dispatches come in solves of `iters` launches; average each launch index

@@ -1,0 +1,66 @@
+"""Host logic of bench.py on the CPU: the per-launch HBM bytes built from
+rocprofv3 counter CSVs (scaled by the calibration copy, grouped into calls),
+and the refusal of more than one GPU."""
+import csv
+import json
+import subprocess
+import sys
+from pathlib import Path
+
+import bench
+
+ROOT = Path(__file__).resolve().parents[1]
+GIB = float(1 << 30)
+
+
+def write_csv(path, counter, dispatches):
+    """dispatches: (kernel name, counter value in KiB) in dispatch order"""
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for i, (name, kib) in enumerate(dispatches):
+            w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": name, "Counter_Name": counter, "Counter_Value": kib})
+
+
+def calibration(counter_kib):
+    return [("__amd_rocclr_copyBuffer", 0.0), ("__amd_rocclr_copyBuffer", counter_kib)]
+
+
+def test_dense_traffic_sums_each_scan(tmp_path):
+    """A scan is every dense launch from one transfer launch to the next,
+    whatever their number; other kernels in between are not counted."""
+    scan_f = [("void pararnn::dense_chunk_kernel<true>(pararnn::DenseArgs)", 10.0),
+              ("pararnn::dense_carry_kernel(pararnn::DenseArgs)", 1.0),
+              ("pararnn::ws_clear_kernel(...)", 99.0),
+              ("void pararnn::dense_apply_kernel<true>(pararnn::DenseArgs)", 20.0)]
+    scan_w = [(n, v) for n, v in zip([d[0] for d in scan_f], [5.0, 0.0, 77.0, 2.0])]
+    # FETCH_SIZE reads half of the copy's bytes, WRITE_SIZE all of them
+    write_csv(tmp_path / "f.csv", "FETCH_SIZE", calibration(GIB / 2 / 1024) + scan_f * 2)
+    write_csv(tmp_path / "w.csv", "WRITE_SIZE", calibration(GIB / 1024) + scan_w * 2)
+    d = bench.traffic_from_counters("dense_case", str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), 1,
+                                    kernel="dense")
+    assert d["fetch_scale"] == 2.0 and d["write_scale"] == 1.0
+    assert d["per_launch"] == [{"fetch": 31 * 1024 * 2.0, "write": 7 * 1024 * 1.0}]
+    assert d["bytes_per_launch"] == 31 * 2048 + 7 * 1024
+
+
+def test_iteration_traffic_averages_each_launch_index(tmp_path):
+    """Per-iteration launches come in solves of K; launch k is averaged over
+    the solves, and bytes_per_launch is the mean over k."""
+    name = "void pararnn::newton_iter_kernel<...>(pararnn::IterArgs)"
+    f = [(name, v) for v in (1.0, 2.0, 3.0, 3.0, 4.0, 5.0)]
+    w = [(name, v) for v in (6.0, 6.0, 6.0, 8.0, 8.0, 8.0)]
+    write_csv(tmp_path / "f.csv", "FETCH_SIZE", calibration(GIB / 1024) + f)
+    write_csv(tmp_path / "w.csv", "WRITE_SIZE", calibration(GIB / 1024) + w)
+    d = bench.traffic_from_counters("iter_case", str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), 3)
+    assert [x["fetch"] for x in d["per_launch"]] == [2048.0, 3072.0, 4096.0]
+    assert [x["write"] for x in d["per_launch"]] == [7168.0] * 3
+    assert d["bytes_per_launch"] == 3072.0 + 7168.0
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, str(ROOT / "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       cwd=ROOT, timeout=300)
+    assert r.returncode != 0
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert msg["n_gpus"] == 2 and "one GPU" in msg["error"]
