@@ -1,9 +1,16 @@
-"""Build the HIP C-ABI library libpararnn.so for gfx950 (in-tree)."""
+"""Build the HIP C-ABI library libpararnn.so for gfx950 (in-tree).
+
+Two compiler passes: the device pass compiles the kernels for gfx950 into an
+offload bundle, with packed fp32 instructions (v_pk_*_f32) switched off; the
+host pass compiles the launch code and embeds that bundle. The target-feature
+flag goes to the device pass only, where it exists.
+"""
 from __future__ import annotations
 
 import os
 import subprocess
 import sys
+import tempfile
 from pathlib import Path
 
 PKG = Path(__file__).resolve().parent
@@ -11,16 +18,10 @@ CSRC = PKG / "csrc"
 LIB = PKG / "libpararnn.so"
 ARCH = "gfx950"
 
-HIPCC_FLAGS = [
-    f"--offload-arch={ARCH}",
-    "-O3",
-    "-std=c++17",
-    "-fPIC",
-    "-shared",
-    "-Wall",
-    # no packed fp32 (v_pk_*_f32) instructions in the device code
-    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-]
+COMMON_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-Wall"]
+# no packed fp32 (v_pk_*_f32) instructions in the device code
+DEVICE_FLAGS = ["--cuda-device-only", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+HOST_FLAGS = ["--cuda-host-only", "-fPIC", "-shared"]
 
 
 def hipcc() -> str:
@@ -28,14 +29,24 @@ def hipcc() -> str:
     return str(Path(rocm) / "bin" / "hipcc")
 
 
+def build_one(src: Path, out: Path, verbose: bool = False, extra_flags=()) -> Path:
+    """Compile one .hip source into a shared library at `out`."""
+    tmp = out.with_name(out.name + ".tmp")
+    with tempfile.TemporaryDirectory() as td:
+        fatbin = Path(td) / (src.stem + ".hipfb")
+        dev = [hipcc(), *COMMON_FLAGS, *DEVICE_FLAGS, *extra_flags, str(src), "-o", str(fatbin)]
+        host = [hipcc(), *COMMON_FLAGS, *HOST_FLAGS, *extra_flags, "-Xclang", "-fcuda-include-gpubinary",
+                "-Xclang", str(fatbin), str(src), "-o", str(tmp)]
+        for cmd in (dev, host):
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
 def build(verbose: bool = False, extra_flags=()) -> Path:
-    tmp = LIB.with_name(LIB.name + ".tmp")
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, str(CSRC / "pararnn.hip"), "-o", str(tmp)]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    return build_one(CSRC / "pararnn.hip", LIB, verbose, extra_flags)
 
 
 if __name__ == "__main__":
