@@ -21,7 +21,9 @@
  * Conventions for every call:
  *  - All array pointers are DEVICE pointers to caller-owned, contiguous,
  *    row-major buffers. The library never allocates, frees or keeps a pointer
- *    after returning; all scratch lives in the caller's workspace `ws`.
+ *    after returning; all scratch lives in the caller's workspace `ws` (the
+ *    one exception, pararnn_solve_gru_scratch, uses a scratch array built into
+ *    the library instead).
  *  - Layouts: u [B][L][G][D] (fp32 or bf16 per opts.u_dtype), a [G][D] fp32,
  *    states h, c [B][L][D] fp32, initial states h0, c0 [B][D] fp32 (NULL means
  *    zero), dh [B][L][D] fp32, du [B][L][G][D] fp32 (always fp32).
@@ -53,6 +55,7 @@ extern "C" {
 #define PARARNN_EUNSUPPORTED (-2) /* unsupported dtype or misaligned pointer */
 #define PARARNN_EWORKSPACE (-3)   /* ws_bytes smaller than pararnn_workspace_bytes() */
 #define PARARNN_EHIP (-4)         /* a HIP launch or runtime call failed */
+#define PARARNN_ESCRATCH (-5)     /* the built-in scratch of pararnn_solve_gru_scratch is too small */
 
 typedef enum { PARARNN_F32 = 0, PARARNN_BF16 = 1 } pararnn_dtype;
 
@@ -114,6 +117,28 @@ size_t pararnn_workspace_bytes(int32_t cell, int32_t op, const pararnn_opts* o);
 int32_t pararnn_solve_gru(const void* u, const float* a, const float* h0, float* h, void* ws,
                           size_t ws_bytes, const pararnn_opts* o, int32_t* iters,
                           int32_t* converged, float* max_update, void* stream);
+
+/* The ParaGRU forward solve of pararnn_solve_gru for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): no ws / ws_bytes arguments. The workspace
+ * is a scratch array built into the library, one per GPU, of
+ * pararnn_scratch_bytes() bytes (64 MiB), reserved when the library's code
+ * object is loaded on that GPU and held until the process ends. The call
+ * allocates and frees nothing; on its first call on a GPU it looks up the
+ * array's device address (hipGetSymbolAddress) with that GPU current.
+ * Arguments, outputs, asynchrony and numerics are those of pararnn_solve_gru.
+ * Errors: as for pararnn_solve_gru; PARARNN_ESCRATCH, before any HIP call,
+ * when pararnn_workspace_bytes(PARARNN_GRU, PARARNN_OP_SOLVE, o) exceeds the
+ * scratch size. Every call on one GPU uses that GPU's one array, and each
+ * call resets what must start at zero; calls on one GPU must therefore be
+ * ordered (one stream, or synchronised): calls that overlap in time race on
+ * the array and give wrong results. */
+int32_t pararnn_solve_gru_scratch(const void* u, const float* a, const float* h0, float* h,
+                                  const pararnn_opts* o, int32_t* iters, int32_t* converged,
+                                  float* max_update, void* stream);
+
+/* Size in bytes of the built-in scratch of pararnn_solve_gru_scratch. */
+size_t pararnn_scratch_bytes(void);
 
 /* ParaLSTM forward solve: as pararnn_solve_gru with the 2x2 block Jacobian over
  * (c, h). Outputs c and h, both [B][L][D]; max_update is the max over both

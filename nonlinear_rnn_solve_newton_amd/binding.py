@@ -69,6 +69,10 @@ def lib():
         L.pararnn_workspace_bytes.restype = SZ
         L.pararnn_solve_gru.argtypes = [P, P, P, P, P, SZ, OPTP, P, P, P, P]
         L.pararnn_solve_gru.restype = I32
+        L.pararnn_solve_gru_scratch.argtypes = [P, P, P, P, OPTP, P, P, P, P]
+        L.pararnn_solve_gru_scratch.restype = I32
+        L.pararnn_scratch_bytes.argtypes = []
+        L.pararnn_scratch_bytes.restype = SZ
         L.pararnn_solve_lstm.argtypes = [P, P, P, P, P, P, P, SZ, OPTP, P, P, P, P]
         L.pararnn_solve_lstm.restype = I32
         L.pararnn_adjoint.argtypes = [I32, P, P, P, P, P, P, P, P, P, P, P, SZ, OPTP, P]
@@ -185,6 +189,41 @@ def solve(cell: str, u: torch.Tensor, a: torch.Tensor, *, h0=None, c0=None, iter
     res = dict(out)
     res.update(iters=it, converged=conv, max_update=mu, ws=ws)
     return res
+
+
+def scratch_bytes() -> int:
+    """Size of the scratch array built into the library (pararnn_solve_gru_scratch)."""
+    return int(lib().pararnn_scratch_bytes())
+
+
+def solve_gru_scratch(u: torch.Tensor, a: torch.Tensor, *, h0=None, iters: int = 3, tol: float = 1e-4,
+                      early_exit: bool = False, out: Optional[torch.Tensor] = None, it=None, conv=None,
+                      mu=None, events: Optional[Sequence[int]] = None, schedule: str = "auto"):
+    """ParaGRU solve through pararnn_solve_gru_scratch: the library's built-in
+    scratch replaces the workspace, so the call itself allocates nothing on the
+    device when out, it, conv and mu are passed in. Returns dict(h, iters,
+    converged, max_update)."""
+    _dev(u, "u")
+    if u.dim() != 4 or u.shape[2] != 3:
+        raise PararnnError("u must be [B][L][3][D]")
+    B, L, _, D = u.shape
+    dev = u.device
+    _dev(a, "a", torch.float32, (3, D))
+    _dev(h0, "h0", torch.float32, (B, D))
+    if out is None:
+        out = torch.empty(B, L, D, dtype=torch.float32, device=dev)
+    _dev(out, "h", torch.float32, (B, L, D))
+    it = torch.empty(1, dtype=torch.int32, device=dev) if it is None else _dev(it, "iters", torch.int32, (1,))
+    conv = (torch.empty(B, dtype=torch.int32, device=dev) if conv is None
+            else _dev(conv, "converged", torch.int32, (B,)))
+    mu = (torch.empty(iters, B, dtype=torch.float32, device=dev) if mu is None
+          else _dev(mu, "max_update", torch.float32, (iters, B)))
+    o, keep = make_opts(B, L, D, iters, tol, early_exit, _u_dtype(u), events, schedule)
+    st = lib().pararnn_solve_gru_scratch(_ptr(u), _ptr(a), _ptr(h0), _ptr(out), ctypes.byref(o), _ptr(it),
+                                         _ptr(conv), _ptr(mu), _stream(dev))
+    del keep
+    _check(st, "pararnn_solve_gru_scratch")
+    return dict(h=out, iters=it, converged=conv, max_update=mu)
 
 
 def solve_gru(u, a, h0=None, **kw):

@@ -7,6 +7,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/pararnn.h"
 #include "adjoint.h"
 #include "newton_fused.h"
@@ -631,6 +633,40 @@ int scan_dense(const float* A, const float* b, const float* s0, float* s, void* 
              : launch(dense_apply_kernel<false>, dim3(nseg), dim3(64), stream, stamps(o, -1, 2), da);
 }
 
+// ---------------------------------------------------------------------------
+// Built-in device scratch for callers that cannot allocate (the scratch
+// variant of the GRU solve). One array per GPU, reserved when the code object
+// is loaded on that GPU and held until the process ends. In host code its name
+// is only a host-side handle: the kernels get the device address found by
+// hipGetSymbolAddress, kept per device.
+constexpr size_t kScratchBytes = static_cast<size_t>(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the device of `stream` (the current device
+// for the null stream). Looked up once per device, with that device current.
+int scratch_ptr(hipStream_t stream, void** out) {
+  int dev = 0;
+  if ((stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev)) != hipSuccess) return PARARNN_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return PARARNN_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return PARARNN_EHIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return PARARNN_EHIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return PARARNN_EHIP;
+    if (e != hipSuccess || !p) return PARARNN_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PARARNN_OK;
+}
+
 }  // namespace
 }  // namespace pararnn
 
@@ -669,6 +705,24 @@ extern "C" int32_t pararnn_solve_gru(const void* u, const float* a, const float*
                                      int32_t* converged, float* max_update, void* stream) {
   return solve(PARARNN_GRU, u, a, nullptr, h0, nullptr, h, ws, ws_bytes, o, iters, converged, max_update,
                static_cast<hipStream_t>(stream));
+}
+
+extern "C" size_t pararnn_scratch_bytes(void) { return kScratchBytes; }
+
+extern "C" int32_t pararnn_solve_gru_scratch(const void* u, const float* a, const float* h0, float* h,
+                                             const pararnn_opts* o, int32_t* iters, int32_t* converged,
+                                             float* max_update, void* stream_) {
+  // every check that needs no device comes first, so that a rejected call
+  // makes no HIP call at all
+  const size_t need = pararnn_workspace_bytes(PARARNN_GRU, PARARNN_OP_SOLVE, o);
+  if (need == 0 || !u || !a || !h) return PARARNN_EINVAL;
+  if (need > kScratchBytes) return PARARNN_ESCRATCH;
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  void* ws = nullptr;
+  const int rc = scratch_ptr(stream, &ws);
+  if (rc) return rc;
+  return solve(PARARNN_GRU, u, a, nullptr, h0, nullptr, h, ws, kScratchBytes, o, iters, converged, max_update,
+               stream);
 }
 
 extern "C" int32_t pararnn_solve_lstm(const void* u, const float* a, const float* c0, const float* h0,
@@ -750,6 +804,7 @@ extern "C" const char* pararnn_strerror(int32_t status) {
     case PARARNN_EUNSUPPORTED: return "unsupported dtype or misaligned pointer";
     case PARARNN_EWORKSPACE: return "workspace smaller than pararnn_workspace_bytes()";
     case PARARNN_EHIP: return "HIP launch or runtime error";
+    case PARARNN_ESCRATCH: return "problem needs more workspace than the built-in scratch holds (pararnn_scratch_bytes())";
     default: return "unknown status";
   }
 }

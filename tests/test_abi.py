@@ -21,7 +21,7 @@ def test_every_declared_symbol_is_exported(lib):
     names = b.header_functions()
     assert set(names) == {"pararnn_workspace_bytes", "pararnn_solve_gru", "pararnn_solve_lstm",
                           "pararnn_adjoint", "pararnn_scan_diag", "pararnn_scan_block2", "pararnn_scan_dense",
-                          "pararnn_strerror"}
+                          "pararnn_strerror", "pararnn_solve_gru_scratch", "pararnn_scratch_bytes"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -31,7 +31,7 @@ def test_status_codes_match_header(lib):
     codes = dict((m[0], int(m[1])) for m in re.findall(r"#define (PARARNN_E?[A-Z]+) \((-?\d+)\)", text))
     codes["PARARNN_OK"] = int(re.search(r"#define PARARNN_OK (\d+)", text).group(1))
     assert codes == {"PARARNN_OK": 0, "PARARNN_EINVAL": -1, "PARARNN_EUNSUPPORTED": -2,
-                     "PARARNN_EWORKSPACE": -3, "PARARNN_EHIP": -4}
+                     "PARARNN_EWORKSPACE": -3, "PARARNN_EHIP": -4, "PARARNN_ESCRATCH": -5}
     for v in codes.values():
         assert b.strerror(v) != "unknown status"
     assert b.strerror(7) == "unknown status"
@@ -159,3 +159,26 @@ def test_scan_dense_workspace_and_invalid_arguments(lib):
     assert f(P(1), P(1), None, P(1), P(2), 16, ctypes.byref(o), None) == -3
     assert f(P(1), P(1), None, P(1), ctypes.c_void_p(2 * 4096 + 16), 1 << 40, ctypes.byref(o), None) == -2
     assert f(ctypes.c_void_p(4097), P(1), None, P(1), P(2), 1 << 40, ctypes.byref(o), None) == -2  # misaligned A
+
+
+def test_scratch_variant_rejects_before_any_hip_call(lib):
+    """pararnn_solve_gru_scratch checks sizes and pointers on the host first:
+    a problem whose workspace exceeds the built-in scratch gets ESCRATCH and
+    invalid arguments EINVAL, with no HIP call (this runs without a GPU)."""
+    assert lib.pararnn_scratch_bytes() == 64 << 20
+    P = lambda v: ctypes.c_void_p(v * 4096) if v else None  # noqa: E731  (never dereferenced)
+
+    def call(B, L, D, K=3, u=1, a=1, h=1, schedule="auto"):
+        o, _ = b.make_opts(B, L, D, K, 1e-4, False, b.BF16, None, schedule)
+        return lib.pararnn_solve_gru_scratch(P(u), P(a), None, P(h), ctypes.byref(o), None, None, None, None)
+
+    # the per-iteration schedule of the B=8 L=4096 D=1024 GRU needs a 134 MB state buffer
+    assert _ws(lib, "gru", b.OP_SOLVE, 8, 4096, 1024, 3, "per_iteration") > lib.pararnn_scratch_bytes()
+    assert call(8, 4096, 1024, schedule="per_iteration") == -5
+    assert call(64, 65536, 4096) == -5
+    assert call(0, 8, 4) == -1
+    assert call(2, 8, 4, K=0) == -1
+    assert call(2, 8, 4, u=0) == -1
+    assert call(2, 8, 4, h=0) == -1
+    # the fused B=8 L=4096 D=1024 GRU fits
+    assert 0 < _ws(lib, "gru", b.OP_SOLVE, 8, 4096, 1024, 3) <= lib.pararnn_scratch_bytes()
