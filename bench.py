@@ -1,17 +1,23 @@
-"""Throughput of the 3-Newton ParaGRU / ParaLSTM solve on one MI355X.
+"""Throughput of the 3-Newton ParaLSTM / ParaGRU solve on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-A step is one whole solve over one batch of seeded synthetic inputs already
-resident in HBM: workspace reset, all K Newton iterations in one fused launch
-(the iterate stays on chip between iterations), flag finalisation; for the
-adjoint workload also the reverse-scan launch. Prints one JSON line with the
-throughput in solved state elements (B*L*D) per second; the roofline of the
-fused launch (vector-ALU issue slots per element over its duration, timed with
-HIP events on the stream the kernels run on); the same solve with one launch
-per iteration and its HBM roofline; and the fp64 CPU oracle timed on a bounded
-sample of the same workload. Scan workloads (--workload scan_*) time the
-linear scan alone.
+A step is one whole pass of the hot path over one batch of seeded synthetic
+inputs already resident in HBM. For the default workload (ParaLSTM, B=16,
+L=2048, D=4096, forward solve plus adjoint) that is: workspace reset, all K
+Newton iterations in one fused launch (the iterate stays on chip between
+iterations), flag finalisation, then the reverse-scan adjoint launch giving
+dL/du. The other workloads (--workload NAME) are the forward solve alone, or
+the linear scan alone for the scan_* workloads.
+
+Prints one JSON line: solved state elements (B*L*D) per second over exactly K
+timed steps; the mean, median and minimum step time; per kernel the duration
+stamped by its own dispatch and its roofline (the fused Newton launch against
+the vector-ALU issue peak with its instructions counted by rocprofv3, and
+against HBM with the bytes it moves; the adjoint against HBM), the dominant
+kernel's under "roofline"; the same solve with one launch per iteration;
+same-run device ceilings (a device copy, the measured VALU issue rates); and
+the fp64 CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -21,36 +27,37 @@ import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
 from pathlib import Path
 
 ROOT = Path(__file__).resolve().parent
+PROFILES = ROOT / "profiles"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak
-# vector ALU issue peak without packed fp32: 256 CUs x 64 lanes x 2.4 GHz
-# lane-operations per second (the fp32 vector 157.3 TFLOP/s counts a packed
-# FMA, 4 flops, per lane-operation)
-# fp32 vector issue slots: 256 CUs x 128 lane-slots per clock x 2.4 GHz, the
-# chip's published fp32 vector peak (157.3 TFLOP/s) counted one FMA per slot.
-# Measured on the card: a stream of non-packed v_mul_f32 / v_fma_f32 issues
-# about 108 lane-ops per clock per CU once two or more waves share a SIMD (one
-# wave alone: about 51), and v_exp_f32 / v_rcp_f32 about 31, i.e. four slots.
-PEAK_VALU_TSLOTS = 256 * 128 * 2.4e9 / 1e12
+# Vector-ALU issue peak: the published fp32 vector peak (157.3 TFLOP/s =
+# 256 CUs x 2.4 GHz x 128 FMA lane-slots per clock, 2 flops each) counted in
+# issue slots, one slot per fp32 lane operation.
+PEAK_VALU_TSLOTS = 157.3 / 2.0
+# A transcendental (v_exp_f32, v_rcp_f32) issues at a quarter of the rate.
+TRANS_SLOTS = 4
 PEAK_F32_MATRIX_TFLOPS = 157.3  # MI355X dense fp32 matrix-core peak
 
 
-# VALU issue slots per state element per Newton iteration (cell, Jacobian,
-# scan), transcendentals at four slots each: GRU about 40 VALU + 6
-# transcendental, LSTM about 70 + 10
-def alu_slots(cell: str) -> int:
-    return 63 if cell == "gru" else 110
-
-# algorithmic HBM bytes per state element for one Newton-iteration launch:
-# read the gate inputs (G per element) and, after the first iteration, the
-# previous iterate; write the new iterate (NS fp32 state components).
+# algorithmic HBM bytes per state element for one Newton-iteration launch of
+# the per-iteration schedule: read the gate inputs (G per element) and, after
+# the first iteration, the previous iterate; write the new iterate (NS fp32
+# state components).
 def iter_bytes(cell: str, u_bytes: int, k: int) -> int:
     G, NS = (3, 1) if cell == "gru" else (4, 2)
     return G * u_bytes + NS * 4 * (1 if k == 1 else 2)
+
+
+# the fused launch (all K iterations, iterate on chip): read the gate inputs
+# once, write the final iterate once
+def fused_bytes(cell: str, u_bytes: int) -> int:
+    G, NS = (3, 1) if cell == "gru" else (4, 2)
+    return G * u_bytes + NS * 4
 
 
 # adjoint: read u, the trajectory and dh, write du (fp32)
@@ -60,10 +67,12 @@ def adjoint_bytes(cell: str, u_bytes: int) -> int:
 
 
 def source_digest() -> str:
-    """Digest of the kernel sources with comments and blank lines removed, so
-    that counters stay tied to the code they were taken on, not its comments."""
+    """Digest of the solver's kernel sources with comments and blank lines
+    removed, so that counters stay tied to the code they were taken on, not
+    its comments. The measurement probe (issue_rate.hip) is not included."""
     h = hashlib.sha256()
-    for p in sorted((ROOT / "nonlinear_rnn_solve_newton_amd" / "csrc").glob("*")):
+    csrc = ROOT / "nonlinear_rnn_solve_newton_amd" / "csrc"
+    for p in sorted(list(csrc.glob("*.h")) + [csrc / "pararnn.hip"]):
         text = re.sub(r"/\*.*?\*/", "", p.read_text(), flags=re.S)
         lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines())
         h.update(p.name.encode())
@@ -104,35 +113,57 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
+def stats(v):
+    """mean, median and minimum of a list of times (ms)"""
+    return {"mean": sum(v) / len(v), "median": statistics.median(v), "min": min(v), "max": max(v), "n": len(v)}
+
+
+# ---------------------------------------------------------------------------
+# Counter files under profiles/: per-launch HBM bytes (FETCH_SIZE + WRITE_SIZE)
+# and VALU instruction counts, each tagged with the source digest it was taken
+# on; a file for other sources is ignored.
+
 def traffic_path(workload: str, kernel: str = "newton_iter") -> Path:
-    return ROOT / "profiles" / f"{kernel}_{workload}_traffic.json"
+    return PROFILES / f"{kernel}_{workload}_traffic.json"
+
+
+def valu_path(workload: str, kernel: str = "newton_fused") -> Path:
+    return PROFILES / f"{kernel}_{workload}_valu.json"
+
+
+def load_profile(path: Path, digest: str):
+    if not path.exists():
+        return None
+    try:
+        d = json.loads(path.read_text())
+    except ValueError:
+        return None
+    return d if d.get("source_digest") == digest else None
 
 
 def load_traffic(workload: str, digest: str, kernel: str = "newton_iter"):
     """Counter-measured HBM bytes per launch for the current kernel sources, if profiled."""
-    f = traffic_path(workload, kernel)
-    if not f.exists():
-        return None
-    try:
-        d = json.loads(f.read_text())
-    except ValueError:
-        return None
-    if d.get("source_digest") != digest:
-        return None
-    return d.get("bytes_per_launch")
+    d = load_profile(traffic_path(workload, kernel), digest)
+    return None if d is None else d.get("bytes_per_launch")
+
+
+def _counter_rows(path, counter):
+    import csv
+
+    rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return rows
 
 
 def traffic_from_counters(workload: str, fetch_csv: str, write_csv: str, iters: int,
                           kernel: str = "newton_iter") -> dict:
-    """Per-launch HBM bytes of the Newton-iteration (or scan) kernel from two rocprofv3
-    --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) of
-    `bench.py --copy-calibration`. Each counter is scaled by bytes / counter of
-    the 1 GiB device copy in the same run."""
-    import csv
+    """Per-launch HBM bytes of one kernel from two rocprofv3 --pmc runs
+    (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) of `bench.py
+    --copy-calibration`. Each counter is scaled by bytes / counter of the
+    1 GiB device copy in the same run."""
 
     def read(path, counter):
-        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
-        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        rows = _counter_rows(path, counter)
         copy = [float(r["Counter_Value"]) * 1024 for r in rows
                 if "copyBuffer" in r["Kernel_Name"] and float(r["Counter_Value"]) > 1e5]
         if kernel == "dense":  # one scan = the launches from one transfer launch to the next
@@ -160,70 +191,183 @@ def traffic_from_counters(workload: str, fetch_csv: str, write_csv: str, iters: 
         w = [v * wscale for j, v in enumerate(wi) if j % iters == k]
         per_k.append({"fetch": sum(f) / len(f), "write": sum(w) / len(w)})
     mean = sum(x["fetch"] + x["write"] for x in per_k) / iters
-    return {"workload": workload, "source_digest": source_digest(), "bytes_per_launch": mean,
-            "per_launch": per_k, "fetch_scale": fscale, "write_scale": wscale,
+    return {"workload": workload, "kernel": f"{kernel}_kernel", "source_digest": source_digest(),
+            "bytes_per_launch": mean, "per_launch": per_k, "fetch_scale": fscale, "write_scale": wscale,
             "calibration": "1 GiB hipMemcpy device copy (__amd_rocclr_copyBuffer) in the same run"}
 
 
-def write_stats_summary(workload: str, stats_csv: str) -> str:
+# SQ counters of one --pmc pass: instruction counts are per wave (64 lanes).
+VALU_COUNTERS = ("SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32")
+
+
+def valu_from_counters(workload: str, csv_path: str, elements: int, iters: int, trans_in_valu: bool,
+                       kernel: str = "newton_fused") -> dict:
+    """VALU issue slots per launch of one kernel from a rocprofv3 --pmc run with
+    SQ_INSTS_VALU and SQ_INSTS_VALU_TRANS_F32 (wave instructions per
+    dispatch): lane slots = 64 x (regular + TRANS_SLOTS x transcendental).
+    trans_in_valu says whether SQ_INSTS_VALU already counts the
+    transcendentals (measured with the issue-rate probe's exp-only kernel)."""
+    per = {}
+    for c in VALU_COUNTERS:
+        vals = [float(r["Counter_Value"]) for r in _counter_rows(csv_path, c) if f"{kernel}_kernel" in r["Kernel_Name"]]
+        if not vals:
+            raise ValueError(f"no {c} rows for {kernel}_kernel in {csv_path}")
+        per[c] = sum(vals) / len(vals)
+    trans = per["SQ_INSTS_VALU_TRANS_F32"]
+    regular = per["SQ_INSTS_VALU"] - (trans if trans_in_valu else 0.0)
+    slots = 64.0 * (regular + TRANS_SLOTS * trans)
+    return {"workload": workload, "kernel": f"{kernel}_kernel", "source_digest": source_digest(),
+            "per_launch": per, "trans_in_valu": trans_in_valu, "elements": elements, "iterations": iters,
+            "regular_per_element_iteration": 64.0 * regular / (elements * iters),
+            "trans_per_element_iteration": 64.0 * trans / (elements * iters),
+            "slots_per_launch": slots, "slots_per_element_iteration": slots / (elements * iters),
+            "slot_rule": f"64 lanes x (regular VALU + {TRANS_SLOTS} x transcendental) wave instructions"}
+
+
+def write_stats_summary(workload: str, stats_csv: str, command: str) -> str:
     """profiles/<workload>_kernel_stats.md from rocprofv3 --kernel-trace --stats output."""
     import csv
 
     rows = list(csv.DictReader(open(stats_csv)))
     lines = [f"# rocprofv3 kernel statistics: {workload}", "",
-             "Command (on the MI355X box, from /tmp with TMPDIR=/tmp):", "",
-             f"    rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o run -- "
-             f"python3 <repo>/bench.py --workload {workload} --steps 5 --warmup 2 --no-cpu-baseline", "",
+             "Command (on the MI355X box, from /tmp with TMPDIR=/tmp):", "", f"    {command}", "",
              f"Kernel sources digest: {source_digest()} (bench.py source_digest()).", "",
              "| kernel | calls | average ns | min ns | max ns | % time |", "|---|---|---|---|---|---|"]
     for r in rows:
-        lines.append(f"| `{r['Name'][:100]}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | "
+        lines.append(f"| `{r['Name'][:110]}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | "
                      f"{r['MaxNs']} | {float(r['Percentage']):.2f} |")
     text = "\n".join(lines) + "\n"
-    (ROOT / "profiles" / f"{workload}_kernel_stats.md").write_text(text)
+    (PROFILES / f"{workload}_kernel_stats.md").write_text(text)
     return text
 
 
-def cpu_baseline(w, x, iters, target_s=12.0):
-    """fp64 oracle Newton solve on a channel sample of the same workload."""
+# ---------------------------------------------------------------------------
+# Same-run device ceilings: a device-to-device copy through torch, and the
+# VALU issue rates of the measurement kernels (issue_rate.hip).
+
+def device_ceilings(dev, hip):
+    import torch
+
+    out = {}
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / 5
+    gbs = 2 * src.numel() * 4 / (ms * 1e-3) / 1e9
+    out["device_copy"] = {"gbs": gbs, "frac": gbs / PEAK_HBM_GBS, "bytes": 2 * src.numel() * 4,
+                          "what": "torch copy_ of 1 GiB, read + write bytes"}
+    del src, dst
+    out["valu_issue"] = issue_rates(dev, hip)
+    return out
+
+
+def issue_rates(dev, hip, waves_per_simd=(1, 2, 3, 8)):
+    """Lane operations per second of the issue-rate kernels, per waves per
+    SIMD (all 256 CUs x 4 SIMDs filled): plain fp32 FMA, v_exp_f32, and the
+    sigmoid-shaped mix, the last in issue slots (transcendentals at
+    TRANS_SLOTS)."""
+    import torch
+
+    from nonlinear_rnn_solve_newton_amd import build
+
+    if not build.ISSUE_LIB.exists():
+        return None
+    L = ctypes.CDLL(str(build.ISSUE_LIB))
+    L.issue_rate_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_float,
+                                    ctypes.c_void_p, ctypes.c_void_p]
+    steps = L.issue_rate_steps_per_trip()
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    ev = hip.create(2)
+    rec = hip.hip.hipEventRecord
+    rec.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    res = {}
+    for wps in waves_per_simd:
+        blocks = 256 * wps  # 4 waves per block: one per SIMD
+        buf = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+        row = {}
+        for kind, name, iters, per_step in ((0, "fma", 2000, 1), (1, "exp", 500, 1), (2, "sigmoid_mix", 400, 4)):
+            L.issue_rate_launch(kind, blocks, 10, 0.999, 1e-3, ctypes.c_void_p(buf.data_ptr()), stream)
+            rec(ctypes.c_void_p(ev[0]), stream)
+            if L.issue_rate_launch(kind, blocks, iters, 0.999, 1e-3, ctypes.c_void_p(buf.data_ptr()), stream):
+                raise RuntimeError("issue_rate_launch failed")
+            rec(ctypes.c_void_p(ev[1]), stream)
+            t = hip.ms(ev[0], ev[1]) * 1e-3
+            lane_steps = blocks * 256.0 * iters * steps
+            if kind == 2:  # 2 regular + 2 transcendental instructions per step
+                row[name] = {"lane_ops_per_s": lane_steps * 4 / t,
+                             "slots_per_s": lane_steps * (2 + 2 * TRANS_SLOTS) / t}
+                row[name]["slot_frac_of_peak"] = row[name]["slots_per_s"] / (PEAK_VALU_TSLOTS * 1e12)
+            else:
+                row[name] = {"lane_ops_per_s": lane_steps * per_step / t,
+                             "per_clock_per_cu_at_2p4GHz": lane_steps * per_step / t / (256 * 2.4e9)}
+        res[f"{wps}_waves_per_simd"] = row
+    hip.destroy(ev)
+    return res
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle as it stands, on a channel sample.
+
+def cpu_baseline(w, x, iters, target_s=15.0, single_s=3.0):
+    """The fp64 oracle on a sample of channels (b, d) of the same workload, full
+    L: its Newton solve (K iterations) and, for the adjoint workload, its BPTT
+    along that solve; plus the sequential recurrence, and a one-thread run."""
     from nonlinear_rnn_solve_newton_amd.workloads import gather_channels, sample_channels
     from oracle import oracle as O
 
     nthreads = O.default_threads()
     BD = w.B * w.D
 
-    def run(n):
+    def run(n, threads):
         ch = sample_channels(w.B, w.D, n, seed=99)
         u = gather_channels(x.u, ch, w.D)
         a = x.a[:, ch % w.D].contiguous()
         t0 = time.perf_counter()
-        O.newton(w.cell, u, a, K=iters, nthreads=nthreads)
+        S, _ = O.newton(w.cell, u, a, K=iters, nthreads=threads)
         t1 = time.perf_counter()
-        O.seq(w.cell, u, a, nthreads=nthreads)
+        if w.adjoint:
+            O.adjoint(w.cell, u, a, S, gather_channels(x.dh, ch, w.D), nthreads=threads)
         t2 = time.perf_counter()
-        return len(ch), t1 - t0, t2 - t1
+        O.seq(w.cell, u, a, nthreads=threads)
+        t3 = time.perf_counter()
+        return len(ch), t1 - t0, t2 - t1, t3 - t2
 
-    n0 = min(BD, max(nthreads, 16))
-    n, t_newton, _ = run(n0)
-    per_chan = t_newton / n
-    n = int(min(BD, max(n0, target_s / max(per_chan, 1e-9))))
-    n = max(nthreads, n - n % max(nthreads, 1)) if n < BD else n
-    n, t_newton, t_seq = run(n)
+    def scaled(threads, target):
+        n0 = min(BD, max(threads, 16))
+        n, tn, ta, _ = run(n0, threads)
+        per_chan = (tn + ta) / n
+        n = int(min(BD, max(n0, target / max(per_chan, 1e-9))))
+        n = max(threads, n - n % max(threads, 1)) if n < BD else n
+        return run(n, threads)
+
+    n, tn, ta, ts = scaled(nthreads, target_s)
     elems = n * w.L
-    return {
-        "value": elems / t_newton,
-        "unit": "elems/s",
-        "cores": nthreads,
-        "kind": "oracle",
-        "sample": f"{n} of {BD} channels (b, d) over the full L={w.L}, {iters} fp64 Newton iterations; "
-                  f"{t_newton:.2f} s",
-        "sequential_value": elems / t_seq,
-    }
+    what = f"{iters} fp64 Newton iterations" + (" + BPTT along them" if w.adjoint else "")
+    res = {"value": elems / (tn + ta), "unit": "elems/s", "cores": nthreads, "kind": "oracle",
+           "sample": f"{n} of {BD} channels (b, d) over the full L={w.L}, {what}; {tn + ta:.2f} s",
+           "newton_value": elems / tn, "sequential_value": elems / ts}
+    if w.adjoint:
+        res["adjoint_value"] = elems / ta
+    n1, tn1, ta1, ts1 = scaled(1, single_s)
+    res["single_thread"] = {"value": n1 * w.L / (tn1 + ta1), "cores": 1,
+                            "sample": f"{n1} channels over the full L={w.L}, {what}; {tn1 + ta1:.2f} s",
+                            "sequential_value": n1 * w.L / ts1}
+    return res
 
 
-# linear scan alone: read NS*NS coefficient planes and NS input planes, write
-# NS state planes, fp32
+# ---------------------------------------------------------------------------
+# The linear scan alone and the dense recurrence (the scan tier).
+
 def scan_bytes(ns: int) -> int:
+    """read NS*NS coefficient planes and NS input planes, write NS state planes, fp32"""
     return 4 * (ns * ns + 2 * ns)
 
 
@@ -249,6 +393,31 @@ def cpu_baseline_scan(w, x, target_s=12.0):
             "sample": f"{nb} of {w.B} batch rows (all D={w.D}, full L={w.L}), fp64 loop; {t:.2f} s"}
 
 
+def timed_steps(step, steps, warmup):
+    """warm-up, then exactly `steps` steps between two synchronisations (ms per
+    step from events on the stream the launches go to), then the same number
+    of steps each bracketed by events, for the median and minimum"""
+    import torch
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / steps
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record()
+    for i in range(steps):
+        step()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    return ms_step, stats([evs[i].elapsed_time(evs[i + 1]) for i in range(steps)])
+
+
 def bench_scan_dense(w, args):
     """The dense recurrence (pararnn_scan_dense): chunk transfers on the matrix
     cores, carries, then the recurrence per chunk."""
@@ -263,21 +432,12 @@ def bench_scan_dense(w, args):
     ev = hip.create(3)
     first = binding.scan_dense(A, b, s0)
     ws, out = first["ws"], first["s"]
-    for _ in range(args.warmup):
-        binding.scan_dense(A, b, s0, out=out, ws=ws)
-    torch.cuda.synchronize()
+    step = lambda: binding.scan_dense(A, b, s0, out=out, ws=ws)  # noqa: E731
+    ms_step, step_stats = timed_steps(step, args.steps, args.warmup)
     kms = []
     for _ in range(args.steps):
         binding.scan_dense(A, b, s0, out=out, ws=ws, events=ev)
         kms.append(hip.ms(ev[1], ev[2]))
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        binding.scan_dense(A, b, s0, out=out, ws=ws)
-    stop.record()
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(stop) / args.steps
     t = sum(kms) / len(kms)
     steps = w.B * w.L
     nbytes = steps * (w.n * w.n + 2 * w.n) * 4  # read A and b once, write s once
@@ -293,18 +453,14 @@ def bench_scan_dense(w, args):
         "roofline": {"bound": "hbm", "kernel": "dense_chunk_kernel + dense_carry_kernel + dense_apply_kernel",
                      "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                      "traffic": load_traffic(w.name, source_digest(), "dense"),
-                     "algorithmic_bytes_per_launch": [nbytes], "launch_ms": [t]},
+                     "algorithmic_bytes_per_launch": nbytes, "launch_ms": stats(kms)},
         "matrix_cores": {"achieved": flops / (t * 1e-3) / 1e12, "peak": PEAK_F32_MATRIX_TFLOPS,
                          "unit": "TFLOP/s", "frac": flops / (t * 1e-3) / 1e12 / PEAK_F32_MATRIX_TFLOPS},
-        "timing": {"scan_ms": t, "source_digest": source_digest()},
+        "timing": {"step_ms": step_stats, "scan_ms": stats(kms), "source_digest": source_digest()},
     }
     if args.copy_calibration:
-        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        result["copy_calibration_bytes"] = src.numel() * 4
+        copy_calibration(dev)
+        result["copy_calibration_bytes"] = 1 << 30
     if not args.no_cpu_baseline:
         from oracle import oracle as O
         nthreads = O.default_threads()
@@ -317,6 +473,18 @@ def bench_scan_dense(w, args):
     hip.destroy(ev)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def copy_calibration(dev):
+    """A plain 1 GiB device copy (hipMemcpy's copy kernel), whose counters scale
+    the FETCH_SIZE / WRITE_SIZE readings of the same run."""
+    import torch
+
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
 
 
 def bench_scan(w, args):
@@ -332,55 +500,34 @@ def bench_scan(w, args):
     ev = hip.create(3)
     first = binding.scan(A, b, s0)
     ws, out = first["ws"], first["s"]
-    for _ in range(args.warmup):
-        binding.scan(A, b, s0, out=out, ws=ws)
-    torch.cuda.synchronize()
+    step = lambda: binding.scan(A, b, s0, out=out, ws=ws)  # noqa: E731
+    ms_step, step_stats = timed_steps(step, args.steps, args.warmup)
     scan_ms, clear_ms = [], []
     for _ in range(args.steps):
         binding.scan(A, b, s0, out=out, ws=ws, events=ev)
         clear_ms.append(hip.ms(ev[0], ev[1]))
         scan_ms.append(hip.ms(ev[1], ev[2]))
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        binding.scan(A, b, s0, out=out, ws=ws)
-    stop.record()
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(stop) / args.steps
-    mean = lambda v: sum(v) / len(v)  # noqa: E731
-    kms = mean(scan_ms)
+    kms = sum(scan_ms) / len(scan_ms)
     nbytes = scan_bytes(w.ns) * w.N
     achieved = nbytes / (kms * 1e-3) / 1e9
     digest = source_digest()
     result = {
         "metric": "scanned state elems/s (B*L*D) of the linear scan s_l = A_l s_{l-1} + b_l",
-        "value": w.N / (ms_step * 1e-3),
-        "unit": "elems/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
+        "value": w.N / (ms_step * 1e-3), "unit": "elems/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32",
         "data": "synthetic (seeded; A ~ U(-0.95, 0.95) per block row sum, b, s0 ~ N(0,1))",
         "config": {"workload": w.name, "block": "diag" if w.ns == 1 else "2x2", "B": w.B, "L": w.L, "D": w.D},
         "roofline": {"bound": "hbm", "kernel": "scan_kernel", "achieved": achieved, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                      "traffic": load_traffic(w.name, digest, "scan"),
-                     "algorithmic_bytes_per_launch": [nbytes], "launch_ms": [kms]},
+                     "algorithmic_bytes_per_launch": nbytes, "launch_ms": stats(scan_ms)},
         # reset: from the marker before the workspace reset to the scan's start
-        "timing": {"reset_to_launch_ms": mean(clear_ms), "scan_ms": kms, "source_digest": digest},
+        "timing": {"step_ms": step_stats, "reset_to_launch_ms": stats(clear_ms), "source_digest": digest},
     }
     if args.copy_calibration:
-        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        result["copy_calibration_bytes"] = src.numel() * 4
+        copy_calibration(dev)
+        result["copy_calibration_bytes"] = 1 << 30
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_scan(w, x)
     hip.destroy(ev)
@@ -404,16 +551,7 @@ def bench_generic(w, args):
     else:
         run = lambda: generic.newton_solve(lambda s, uu: generic.lstm_step(s, uu, a), u,  # noqa: E731
                                            B=w.B, L=w.L, D=w.D, iters=w.iters, block=2)
-    for _ in range(args.warmup):
-        run()
-    torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(args.steps):
-        run()
-    stop.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / args.steps
+    ms, st = timed_steps(run, args.steps, args.warmup)
     print(json.dumps({
         "metric": "solved state elems/s (B*L*D) per 3-Newton solve, generic-cell tier",
         "value": w.N / (ms * 1e-3), "unit": "elems/s", "n_gpus": 1, "steps": args.steps,
@@ -421,70 +559,35 @@ def bench_generic(w, args):
         "vs_baseline": None, "dtype": "f32", "data": "synthetic (same inputs as the fused workload)",
         "config": {"workload": w.name, "tier": "generic: torch cell, torch.func.jvp Jacobian, "
                    "pararnn_scan_diag / pararnn_scan_block2 per iteration"},
+        "timing": {"step_ms": st},
     }), flush=True)
     return 0
 
 
-def main(argv=None):
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default=None)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--generic", action="store_true",
-                    help="run the workload's cell through the generic-cell tier (torch cell + forward-mode "
-                         "AD Jacobian + the library's scan) instead of the fused kernels")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 1 GiB device copy (counter calibration for profiling)")
-    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write profiles/newton_iter_<workload>_traffic.json from rocprofv3 counter CSVs")
-    ap.add_argument("--stats-summary", metavar="KERNEL_STATS_CSV",
-                    help="write profiles/<workload>_kernel_stats.md from a rocprofv3 --stats CSV")
-    args = ap.parse_args(argv)
-    sys.path.insert(0, str(ROOT))
-    from nonlinear_rnn_solve_newton_amd.workloads import DENSE_WORKLOADS, HEADLINE, SCAN_WORKLOADS, WORKLOADS
-    name = args.workload or HEADLINE
-    if name not in WORKLOADS and name not in SCAN_WORKLOADS and name not in DENSE_WORKLOADS:
-        print(json.dumps({"error": f"unknown workload {name}",
-                          "workloads": sorted(WORKLOADS) + sorted(SCAN_WORKLOADS) + sorted(DENSE_WORKLOADS)}))
-        return 2
-    if args.stats_summary:
-        print(write_stats_summary(name, args.stats_summary))
-        return 0
-    if args.traffic_from:
-        if name in SCAN_WORKLOADS:
-            d = traffic_from_counters(name, *args.traffic_from, iters=1, kernel="scan")
-            traffic_path(name, "scan").write_text(json.dumps(d, indent=1) + "\n")
-        elif name in DENSE_WORKLOADS:
-            d = traffic_from_counters(name, *args.traffic_from, iters=1, kernel="dense")
-            traffic_path(name, "dense").write_text(json.dumps(d, indent=1) + "\n")
-        else:
-            d = traffic_from_counters(name, *args.traffic_from, iters=WORKLOADS[name].iters)
-            traffic_path(name).write_text(json.dumps(d, indent=1) + "\n")
-            print(json.dumps(d))
-            d = traffic_from_counters(name, *args.traffic_from, iters=1, kernel="newton_fused")
-            traffic_path(name, "newton_fused").write_text(json.dumps(d, indent=1) + "\n")
-        print(json.dumps(d))
-        return 0
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "the library runs on one GPU; sharding across GPUs is described in the "
-                                   "design notes, not implemented", "n_gpus": args.gpus}))
-        return 2
+# ---------------------------------------------------------------------------
+# The Newton solve (and adjoint) workloads.
 
-    if name in SCAN_WORKLOADS:
-        return bench_scan(SCAN_WORKLOADS[name], args)
-    if name in DENSE_WORKLOADS:
-        return bench_scan_dense(DENSE_WORKLOADS[name], args)
-    if args.generic:
-        return bench_generic(WORKLOADS[name], args)
+def kernel_record(name, bound, ms, work, unit, peak, traffic=None, **extra):
+    """One kernel's roofline: `work` algorithmic units (bytes or issue slots)
+    per launch over its mean launch duration."""
+    if work is None:
+        achieved = None
+    elif unit == "GB/s":
+        achieved = work / (ms["mean"] * 1e-3) / 1e9
+    else:
+        achieved = work / (ms["mean"] * 1e-3) / 1e12
+    rec = {"bound": bound, "kernel": name, "achieved": achieved, "peak": peak, "unit": unit,
+           "frac": None if achieved is None else achieved / peak, "traffic": traffic, "launch_ms": ms}
+    rec.update(extra)
+    return rec
 
+
+def bench_solve(w, args):
     import torch
 
     from nonlinear_rnn_solve_newton_amd import binding
     from nonlinear_rnn_solve_newton_amd.workloads import workload_inputs
 
-    w = WORKLOADS[name]
     K = w.iters
     dev = torch.device("cuda:0")
     x = workload_inputs(w)
@@ -496,11 +599,11 @@ def main(argv=None):
     hip = HipEvents()
     ev = hip.create(K + 2)
     ev_adj = hip.create(3) if w.adjoint else None
-    mean = lambda v: sum(v) / len(v)  # noqa: E731
 
     def time_schedule(schedule):
-        """One schedule of the solve (plus the adjoint for the adjoint workload):
-        per-step time without events, and per-kernel times from events."""
+        """One schedule of the solve (plus the adjoint for the adjoint
+        workload): step times without events, then per-kernel durations
+        stamped by the launches' own dispatches."""
         first = binding.solve(w.cell, u, a, iters=K, schedule=schedule)
         ws, out = first["ws"], {k: first[k] for k in ("h", "c") if k in first}
         gadj = binding.adjoint(w.cell, u, a, out["h"], dh, c=out.get("c")) if w.adjoint else None
@@ -511,48 +614,48 @@ def main(argv=None):
                 binding.adjoint(w.cell, u, a, out["h"], dh, c=out.get("c"), ws=gadj["ws"], du=gadj["du"],
                                 events=events_adj)
 
-        for _ in range(args.warmup):
-            step()
-        torch.cuda.synchronize()
+        ms_step, step_stats = timed_steps(step, args.steps, args.warmup)
         launch_ms = [[] for _ in range(K)]
         clear_ms, adj_ms = [], []
         for _ in range(args.steps):
             step(ev, ev_adj)
-            # per-kernel times: read back after the step (events are reused).
-            # The library stamps the launches' own starts and ends into the
-            # events (event 1: the first launch's start; k + 1: the end of
-            # iteration k's launch, for the fused schedule its one launch and
-            # then markers right after it)
+            # event 1: the first launch's start; k + 1: the end of iteration
+            # k's launch (for the fused schedule its one launch, then markers
+            # right after it)
             clear_ms.append(hip.ms(ev[0], ev[1]))
             for k in range(K):
                 launch_ms[k].append(hip.ms(ev[k + 1], ev[k + 2]))
             if w.adjoint:
                 adj_ms.append(hip.ms(ev_adj[1], ev_adj[2]))
-        # the event read-backs synchronise once per step; the step time comes
-        # from a loop without them
-        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        start.record()
-        for _ in range(args.steps):
-            step()
-        stop.record()
-        torch.cuda.synchronize()
-        return {"ms_step": start.elapsed_time(stop) / args.steps, "clear_ms": mean(clear_ms),
-                "launch_ms": [mean(v) for v in launch_ms], "adj_ms": mean(adj_ms) if adj_ms else None,
+        return {"ms_step": ms_step, "step": step_stats, "clear_ms": stats(clear_ms),
+                "launch_ms": [stats(v) for v in launch_ms], "adj_ms": stats(adj_ms) if adj_ms else None,
                 "out": out, "gadj": gadj}
 
     N = w.N
-    bytes_k = [iter_bytes(w.cell, u_bytes, k + 1) * N for k in range(K)]
     digest = source_digest()
     fused = time_schedule("fused")
-    per_it = time_schedule("per_iteration")
-    out, gadj = fused["out"], fused["gadj"]
-    # events 1 and 2: the start and end of the one fused launch, stamped by
-    # its dispatch (the later events are markers recorded after it)
+    per_it = time_schedule("per_iteration") if not args.no_per_iteration else None
+    out = fused["out"]
+
+    # the fused launch: bound by vector-ALU issue; its work is the VALU issue
+    # slots rocprofv3 counted for these sources, and its own HBM bytes (gate
+    # inputs once, final iterate once)
     t_fused = fused["launch_ms"][0]
-    slots = alu_slots(w.cell) * K * N
-    alu = slots / (t_fused * 1e-3) / 1e12
-    hbm_it = sum(bytes_k) / K / (mean(per_it["launch_ms"]) * 1e-3) / 1e9
+    valu = load_profile(valu_path(w.name), digest)
+    fb = fused_bytes(w.cell, u_bytes) * N
+    fused_rec = kernel_record(
+        "newton_fused_kernel", "alu", t_fused, None if valu is None else valu["slots_per_launch"],
+        "T VALU issue slots/s", PEAK_VALU_TSLOTS, load_traffic(w.name, digest, "newton_fused"),
+        valu_counters=None if valu is None else str(valu_path(w.name).relative_to(ROOT)),
+        slots_per_element_iteration=None if valu is None else valu["slots_per_element_iteration"],
+        hbm_own={"bytes_per_launch": fb, "achieved": fb / (t_fused["mean"] * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                 "unit": "GB/s", "frac": fb / (t_fused["mean"] * 1e-3) / 1e9 / PEAK_HBM_GBS})
+    kernels = [fused_rec]
+    if w.adjoint:
+        ab = adjoint_bytes(w.cell, u_bytes) * N
+        kernels.append(kernel_record("adjoint_kernel", "hbm", fused["adj_ms"], ab, "GB/s", PEAK_HBM_GBS,
+                                     load_traffic(w.name, digest, "adjoint"), algorithmic_bytes_per_launch=ab))
+    dominant = max(kernels, key=lambda r: r["launch_ms"]["mean"])
     result = {
         "metric": "solved state elems/s (B*L*D) per 3-Newton solve; HBM GB/s as % of peak",
         "value": N / (fused["ms_step"] * 1e-3),
@@ -565,77 +668,127 @@ def main(argv=None):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "data": "synthetic (seeded; u ~ N(0,1) stored " + w.u_dtype + ", a ~ U(-amax, amax))",
-        "config": {"workload": w.name, "cell": w.cell, "B": w.B, "L": w.L, "D": w.D,
-                   "newton_iters": K, "u_dtype": w.u_dtype, "adjoint": w.adjoint, "schedule": "fused"},
-        # the fused launch keeps the iterate on chip: it moves the gate inputs
-        # once and the final iterate once, and is bound by vector ALU issue
-        "roofline": {
-            "bound": "alu",
-            "kernel": "newton_fused_kernel",
-            "achieved": alu,
-            "peak": PEAK_VALU_TSLOTS,
-            "unit": "T issue-slots/s (fp32 VALU lane-ops, transcendentals at 4 slots)",
-            "frac": alu / PEAK_VALU_TSLOTS,
-            "traffic": load_traffic(w.name, digest, "newton_fused"),
-            "algorithmic_slots_per_launch": slots,
-            "launch_ms": t_fused,
-        },
-        # the same solve in the method's per-iteration form: its algorithmic
-        # bytes (inputs + previous iterate read, new iterate written, per iteration)
-        "hbm_equivalent": {
-            "achieved": sum(bytes_k) / (fused["ms_step"] * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": sum(bytes_k) / (fused["ms_step"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
-            "note": "algorithmic bytes of the per-iteration method per solve / fused solve time"},
-        "per_iteration_schedule": {
-            "ms_per_step": per_it["ms_step"],
-            "roofline": {"bound": "hbm", "kernel": "newton_iter_kernel", "achieved": hbm_it,
-                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": hbm_it / PEAK_HBM_GBS,
-                         "traffic": load_traffic(w.name, digest), "algorithmic_bytes_per_launch": bytes_k,
-                         "launch_ms": per_it["launch_ms"]},
-        },
+        "data": "synthetic (seeded; u ~ N(0,1) stored " + w.u_dtype + ", a ~ U(-amax, amax)"
+                + (", dL/dh ~ N(0,1)" if w.adjoint else "") + ")",
+        "config": {"workload": w.name, "cell": w.cell, "B": w.B, "L": w.L, "D": w.D, "newton_iters": K,
+                   "u_dtype": w.u_dtype, "adjoint": w.adjoint, "schedule": "fused"},
+        "roofline": dominant,
+        "kernels": kernels,
         "timing": {
+            "step_ms": fused["step"],
             # from the marker before the workspace reset to the fused launch's
             # start: the reset kernel and both dispatches
             "reset_to_launch_ms": fused["clear_ms"],
-            "fused_launch_ms": t_fused,
             "source_digest": digest,
         },
     }
-    adj_ms = [fused["adj_ms"]] if w.adjoint else []
+    if per_it is not None:
+        bytes_k = [iter_bytes(w.cell, u_bytes, k + 1) * N for k in range(K)]
+        t_it = [s["mean"] for s in per_it["launch_ms"]]
+        hbm_it = sum(bytes_k) / (sum(t_it) * 1e-3) / 1e9
+        result["per_iteration_schedule"] = {
+            "ms_per_step": per_it["ms_step"], "step_ms": per_it["step"],
+            "roofline": {"bound": "hbm", "kernel": "newton_iter_kernel", "achieved": hbm_it, "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": hbm_it / PEAK_HBM_GBS, "traffic": load_traffic(w.name, digest),
+                         "algorithmic_bytes_per_launch": bytes_k, "launch_ms": per_it["launch_ms"]},
+        }
     if w.adjoint:
         # the same adjoint with the parameter and initial-state gradients
         # (da, ds0) requested: their partials ride in the reverse scan, plus a
         # fixed-order reduction launch
-        gfull = binding.adjoint(w.cell, u, a, out["h"], dh, c=out.get("c"), du=gadj["du"],
-                                want_ds0=True, want_da=True)  # a workspace with room for the da partials
+        gfull = binding.adjoint(w.cell, u, a, out["h"], dh, c=out.get("c"), want_ds0=True, want_da=True)
         grad_ms = []
         for _ in range(args.steps):
             binding.adjoint(w.cell, u, a, out["h"], dh, c=out.get("c"), ws=gfull["ws"], du=gfull["du"],
                             want_ds0=True, want_da=True, events=ev_adj)
             grad_ms.append(hip.ms(ev_adj[1], ev_adj[2]))
         torch.cuda.synchronize()
-        amean = adj_ms[0]
-        result["timing"]["adjoint_ms"] = amean
-        result["timing"]["adjoint_with_da_ds0_ms"] = mean(grad_ms)
-        result["adjoint_roofline"] = {
-            "bound": "hbm", "kernel": "adjoint_kernel",
-            "achieved": adjoint_bytes(w.cell, u_bytes) * N / (amean * 1e-3) / 1e9,
-            "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": adjoint_bytes(w.cell, u_bytes) * N / (amean * 1e-3) / 1e9 / PEAK_HBM_GBS,
-        }
+        result["timing"]["adjoint_with_da_ds0_ms"] = stats(grad_ms)
+        del gfull
+    if not args.no_ceilings:
+        result["device_ceilings"] = device_ceilings(dev, hip)
     if args.copy_calibration:
-        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        result["copy_calibration_bytes"] = src.numel() * 4
+        copy_calibration(dev)
+        result["copy_calibration_bytes"] = 1 << 30
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, x, K)
     hip.destroy(ev + (ev_adj or []))
     print(json.dumps(result), flush=True)
     return 0
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-iteration", action="store_true", help="skip the per-iteration schedule")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the same-run device ceilings")
+    ap.add_argument("--generic", action="store_true",
+                    help="run the workload's cell through the generic-cell tier (torch cell + forward-mode "
+                         "AD Jacobian + the library's scan) instead of the fused kernels")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration for profiling)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/<kernel>_<workload>_traffic.json from rocprofv3 counter CSVs")
+    ap.add_argument("--valu-from", metavar="SQ_CSV",
+                    help="write profiles/newton_fused_<workload>_valu.json from a rocprofv3 --pmc CSV with "
+                         "SQ_INSTS_VALU and SQ_INSTS_VALU_TRANS_F32")
+    ap.add_argument("--trans-in-valu", choices=("yes", "no"), default="yes",
+                    help="whether SQ_INSTS_VALU counts the transcendentals too (with --valu-from)")
+    ap.add_argument("--stats-summary", metavar="KERNEL_STATS_CSV",
+                    help="write profiles/<workload>_kernel_stats.md from a rocprofv3 --stats CSV")
+    ap.add_argument("--stats-command", default=None, help="the rocprofv3 command, for --stats-summary")
+    args = ap.parse_args(argv)
+    sys.path.insert(0, str(ROOT))
+    from nonlinear_rnn_solve_newton_amd.workloads import DENSE_WORKLOADS, HEADLINE, SCAN_WORKLOADS, WORKLOADS
+    name = args.workload or HEADLINE
+    if name not in WORKLOADS and name not in SCAN_WORKLOADS and name not in DENSE_WORKLOADS:
+        print(json.dumps({"error": f"unknown workload {name}",
+                          "workloads": sorted(WORKLOADS) + sorted(SCAN_WORKLOADS) + sorted(DENSE_WORKLOADS)}))
+        return 2
+    if args.stats_summary:
+        cmd = args.stats_command or (
+            "rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o run -- "
+            f"python3 <repo>/bench.py --workload {name} --steps 5 --warmup 2 --no-cpu-baseline --no-ceilings")
+        print(write_stats_summary(name, args.stats_summary, cmd))
+        return 0
+    if args.valu_from:
+        w = WORKLOADS[name]
+        d = valu_from_counters(name, args.valu_from, w.N, w.iters, args.trans_in_valu == "yes")
+        valu_path(name).write_text(json.dumps(d, indent=1) + "\n")
+        print(json.dumps(d))
+        return 0
+    if args.traffic_from:
+        if name in SCAN_WORKLOADS:
+            d = traffic_from_counters(name, *args.traffic_from, iters=1, kernel="scan")
+            traffic_path(name, "scan").write_text(json.dumps(d, indent=1) + "\n")
+        elif name in DENSE_WORKLOADS:
+            d = traffic_from_counters(name, *args.traffic_from, iters=1, kernel="dense")
+            traffic_path(name, "dense").write_text(json.dumps(d, indent=1) + "\n")
+        else:
+            kernels = [("newton_iter", WORKLOADS[name].iters), ("newton_fused", 1)]
+            if WORKLOADS[name].adjoint:
+                kernels.append(("adjoint", 1))
+            for kern, iters in kernels:
+                d = traffic_from_counters(name, *args.traffic_from, iters=iters, kernel=kern)
+                traffic_path(name, kern).write_text(json.dumps(d, indent=1) + "\n")
+                print(json.dumps(d))
+        return 0
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "the library runs on one GPU; sharding across GPUs is described in the "
+                                   "design notes, not implemented", "n_gpus": args.gpus}))
+        return 2
+
+    if name in SCAN_WORKLOADS:
+        return bench_scan(SCAN_WORKLOADS[name], args)
+    if name in DENSE_WORKLOADS:
+        return bench_scan_dense(DENSE_WORKLOADS[name], args)
+    if args.generic:
+        return bench_generic(WORKLOADS[name], args)
+    return bench_solve(WORKLOADS[name], args)
 
 
 if __name__ == "__main__":

@@ -200,6 +200,23 @@ int32_t pararnn_scan_block2(const float* A, const float* b, const float* s0, flo
 int32_t pararnn_scan_dense(const float* A, const float* b, const float* s0, float* s, void* ws,
                            size_t ws_bytes, const pararnn_opts* o, void* stream);
 
+/* The launch plan of a call (host-only; launches nothing), for callers and
+ * tests that need to know how the work is split: a workgroup covers `chunk`
+ * timesteps x `channels` channels, with `vec` channels per lane; `nchunks`
+ * chunks along L are chained by the chunk carry, each chunk row holding
+ * `tiles_per_row` = B x ceil(D / channels) workgroups. `inclusive_only` = 1
+ * when each chunk takes its carry from its neighbour's inclusive carry alone
+ * (a fixed composition order: repeated calls give identical bits); 0 when it
+ * uses the decoupled look-back over chunk aggregates (repeated calls agree to
+ * rounding). `fused` = 1 for the one-launch schedule of a solve. The plan is
+ * the one used when every pointer is 16-byte aligned (narrower alignment
+ * only lowers `vec`). Returns PARARNN_OK, or PARARNN_EINVAL for invalid
+ * options or a NULL plan. */
+typedef struct {
+  int32_t vec, chunk, channels, nchunks, tiles_per_row, inclusive_only, fused;
+} pararnn_plan;
+int32_t pararnn_plan_query(int32_t cell, int32_t op, const pararnn_opts* o, pararnn_plan* plan);
+
 /* Static description of a status code. */
 const char* pararnn_strerror(int32_t status);
 

@@ -48,6 +48,11 @@ class Opts(ctypes.Structure):
 SCHEDULES = {"auto": 0, "fused": 1, "per_iteration": 2}
 
 
+class Plan(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("vec", "chunk", "channels", "nchunks", "tiles_per_row", "inclusive_only", "fused")]
+
+
 def header_functions() -> list[str]:
     """Names of the functions declared in include/pararnn.h."""
     text = HEADER.read_text()
@@ -83,6 +88,8 @@ def lib():
         L.pararnn_scan_block2.restype = I32
         L.pararnn_scan_dense.argtypes = [P, P, P, P, P, SZ, OPTP, P]
         L.pararnn_scan_dense.restype = I32
+        L.pararnn_plan_query.argtypes = [I32, I32, OPTP, ctypes.POINTER(Plan)]
+        L.pararnn_plan_query.restype = I32
         L.pararnn_strerror.argtypes = [I32]
         L.pararnn_strerror.restype = ctypes.c_char_p
         _lib = L
@@ -137,6 +144,18 @@ def workspace_bytes(cell: str, op: int, B: int, L: int, D: int, iters: int = 3,
                     u_dtype: int = BF16) -> int:
     o, _ = make_opts(B, L, D, iters, 1e-4, False, u_dtype)
     return int(lib().pararnn_workspace_bytes(CELLS[cell], op, ctypes.byref(o)))
+
+
+def plan(cell: str, op: int, B: int, L: int, D: int, iters: int = 3, u_dtype: int = BF16,
+         schedule: str = "auto", early_exit: bool = False) -> dict:
+    """The launch plan of a call (pararnn_plan_query; host-only): chunk length,
+    channels per workgroup, chunk count, workgroups per chunk row, and whether
+    the chunk carry runs in the inclusive-only (bitwise-reproducible) mode."""
+    o, _ = make_opts(B, L, D, iters, 1e-4, early_exit, u_dtype, None, schedule)
+    pl = Plan()
+    _check(lib().pararnn_plan_query(CELLS.get(cell, GRU), op, ctypes.byref(o), ctypes.byref(pl)),
+           "pararnn_plan_query")
+    return {n: int(getattr(pl, n)) for n, _ in Plan._fields_}
 
 
 def alloc_workspace(nbytes: int, device) -> torch.Tensor:

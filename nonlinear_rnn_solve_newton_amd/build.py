@@ -16,6 +16,8 @@ from pathlib import Path
 PKG = Path(__file__).resolve().parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libpararnn.so"
+# measurement kernels for the device ceilings bench.py reports (not the solver)
+ISSUE_LIB = PKG / "libissuerate.so"
 ARCH = "gfx950"
 
 COMMON_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-Wall"]
@@ -29,13 +31,14 @@ def hipcc() -> str:
     return str(Path(rocm) / "bin" / "hipcc")
 
 
-def build_one(src: Path, out: Path, verbose: bool = False, extra_flags=()) -> Path:
-    """Compile one .hip source into a shared library at `out`."""
+def build_one(src: Path, out: Path, verbose: bool = False, extra_flags=(), host_flags=()) -> Path:
+    """Compile one .hip source into a shared library at `out`; host_flags go to
+    the host pass only (e.g. a sanitizer build of the host code)."""
     tmp = out.with_name(out.name + ".tmp")
     with tempfile.TemporaryDirectory() as td:
         fatbin = Path(td) / (src.stem + ".hipfb")
         dev = [hipcc(), *COMMON_FLAGS, *DEVICE_FLAGS, *extra_flags, str(src), "-o", str(fatbin)]
-        host = [hipcc(), *COMMON_FLAGS, *HOST_FLAGS, *extra_flags, "-Xclang", "-fcuda-include-gpubinary",
+        host = [hipcc(), *COMMON_FLAGS, *HOST_FLAGS, *extra_flags, *host_flags, "-Xclang", "-fcuda-include-gpubinary",
                 "-Xclang", str(fatbin), str(src), "-o", str(tmp)]
         for cmd in (dev, host):
             if verbose:
@@ -46,6 +49,7 @@ def build_one(src: Path, out: Path, verbose: bool = False, extra_flags=()) -> Pa
 
 
 def build(verbose: bool = False, extra_flags=()) -> Path:
+    build_one(CSRC / "issue_rate.hip", ISSUE_LIB, verbose, extra_flags)
     return build_one(CSRC / "pararnn.hip", LIB, verbose, extra_flags)
 
 

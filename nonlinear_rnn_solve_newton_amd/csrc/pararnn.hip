@@ -152,11 +152,14 @@ struct Layout {
 int nstate(int cell) { return cell == PARARNN_LSTM ? 2 : 1; }
 int ngates(int cell) { return cell == PARARNN_LSTM ? 4 : 3; }
 
+// ceil(a / b) for positive a, b without overflow
+long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
 bool opts_ok(int cell, int op, const pararnn_opts* o) {
   if (!o) return false;
   if (op == PARARNN_OP_SCAN_DENSE)  // the dense scan has no cell; D is the state size
     return o->B >= 1 && o->L >= 1 && o->D >= 1 && o->D <= kDenseMaxN &&
-           static_cast<double>(o->B) * ((o->L + kDenseChunk - 1) / kDenseChunk) < 2.0e9;
+           static_cast<double>(o->B) * ceil_div(o->L, kDenseChunk) < 2.0e9;
   if (op != PARARNN_OP_SOLVE && op != PARARNN_OP_ADJOINT && !is_scan(op)) return false;
   if (!is_scan(op) && cell != PARARNN_GRU && cell != PARARNN_LSTM) return false;  // the scan has no cell
   if (o->B < 1 || o->L < 1 || o->D < 1) return false;
@@ -172,7 +175,7 @@ bool opts_ok(int cell, int op, const pararnn_opts* o) {
     // both schedules of the solve: the per-iteration and the fused geometry
     for (int fused = 0; fused <= (op == PARARNN_OP_SOLVE ? 1 : 0); ++fused) {
       const Geo g = fused ? fused_geo_for(cell, C) : geo_for(cell, op, C);
-      const double wgs = static_cast<double>(o->B) * ((o->D + g.cw - 1) / g.cw) * ((o->L + g.chunk - 1) / g.chunk);
+      const double wgs = static_cast<double>(o->B) * ceil_div(o->D, g.cw) * ceil_div(o->L, g.chunk);
       if (wgs > 2.0e9) return false;
     }
   }
@@ -359,6 +362,29 @@ int launch_scan(bool incl, const ScanArgs& a, hipStream_t s, Stamps t) {
 //   2x2 blocks      +151%    +46%     -6.5%    -8%
 constexpr long long kScanInclTiles = 32;
 
+// The fused kernel's two ways to the chunk carry when the early read misses.
+// Look-back: publish the chunk aggregate and compose predecessors' aggregates
+// back to an inclusive carry. Inclusive only: wait for the predecessor's
+// inclusive carry. Tickets are chunk-major, so a predecessor is one chunk row
+// (B * ntiles_d tickets) ahead. With many tiles per row it runs well ahead and
+// the plain wait is cheaper: it skips the aggregate code (about 16 VGPRs) and
+// the reset of the aggregate descriptors. With few tiles, many chunk rows run
+// at once and the look-back's shortcut through aggregates wins. Same-box
+// measurements, fused solve time, inclusive only against look-back:
+//   tiles per row   16          32          64            256
+//   GRU             +33%        +2%         -4.5%         -5.6%
+//   LSTM            +56%        +15%        -13%          -4.7%
+constexpr long long kInclOnlyTiles = 64;
+
+// The carry mode of a launch: inclusive only (the chunk waits for its
+// neighbour's inclusive carry) where a chunk row has at least the family's
+// threshold of tiles, else the decoupled look-back.
+bool incl_only_for(int cell, int op, bool fused, long long tiles_per_row) {
+  if (is_scan(op)) return tiles_per_row >= kScanInclTiles;
+  if (op == PARARNN_OP_SOLVE && fused) return tiles_per_row >= kInclOnlyTiles;
+  return tiles_per_row >= iter_incl_tiles(cell);
+}
+
 int scan(int ns, const float* A, const float* b, const float* s0, float* s, void* ws, size_t ws_bytes,
          const pararnn_opts* o, hipStream_t stream) {
   const int op = ns == 2 ? PARARNN_OP_SCAN_BLOCK2 : PARARNN_OP_SCAN_DIAG;
@@ -374,7 +400,7 @@ int scan(int ns, const float* A, const float* b, const float* s0, float* s, void
   if (!aligned(ws, kAlign)) return PARARNN_EUNSUPPORTED;
   char* w = static_cast<char*>(ws);
 
-  const bool incl_only = static_cast<long long>(o->B) * y.ntiles_d >= kScanInclTiles;
+  const bool incl_only = incl_only_for(PARARNN_GRU, op, false, static_cast<long long>(o->B) * y.ntiles_d);
   Layout yc = y;  // inclusive only: the aggregate descriptors are never read
   if (incl_only) yc.zero_end = y.agg;
   int rc = record(o, 0, stream);
@@ -437,19 +463,6 @@ int launch_fused_any(int dtype, int C, bool incl, const FusedArgs& a, hipStream_
                                : launch_fused_c<Cell, float>(C, incl, a, s, t);
 }
 
-// The fused kernel's two ways to the chunk carry when the early read misses.
-// Look-back: publish the chunk aggregate and compose predecessors' aggregates
-// back to an inclusive carry. Inclusive only: wait for the predecessor's
-// inclusive carry. Tickets are chunk-major, so a predecessor is one chunk row
-// (B * ntiles_d tickets) ahead. With many tiles per row it runs well ahead and
-// the plain wait is cheaper: it skips the aggregate code (about 16 VGPRs) and
-// the reset of the aggregate descriptors. With few tiles, many chunk rows run
-// at once and the look-back's shortcut through aggregates wins. Same-box
-// measurements, fused solve time, inclusive only against look-back:
-//   tiles per row   16          32          64            256
-//   GRU             +33%        +2%         -4.5%         -5.6%
-//   LSTM            +56%        +15%        -13%          -4.7%
-constexpr long long kInclOnlyTiles = 64;
 
 int solve(int cell, const void* u, const float* a, const float* c0, const float* h0, float* c, float* h,
           void* ws, size_t ws_bytes, const pararnn_opts* o, int32_t* iters, int32_t* converged,
@@ -471,7 +484,7 @@ int solve(int cell, const void* u, const float* a, const float* c0, const float*
 
   const int K = o->max_iters, NS = nstate(cell);
   if (fused) {
-    const bool incl_only = static_cast<long long>(o->B) * y.ntiles_d >= kInclOnlyTiles;
+    const bool incl_only = incl_only_for(cell, PARARNN_OP_SOLVE, true, static_cast<long long>(o->B) * y.ntiles_d);
     Layout yc = y;  // inclusive only: the aggregate descriptors are never read
     if (incl_only) yc.zero_end = y.agg;
     int rc = record(o, 0, stream);
@@ -519,7 +532,7 @@ int solve(int cell, const void* u, const float* a, const float* c0, const float*
 
   int rc = record(o, 0, stream);
   if (rc) return rc;
-  const bool incl_only = static_cast<long long>(o->B) * y.ntiles_d >= iter_incl_tiles(cell);
+  const bool incl_only = incl_only_for(cell, PARARNN_OP_SOLVE, false, static_cast<long long>(o->B) * y.ntiles_d);
   Layout yc = y;  // inclusive only: the aggregate descriptors are never read
   if (incl_only) yc.zero_end = y.agg;
   rc = clear_ws(w, yc, nullptr, 0, stream);
@@ -580,7 +593,7 @@ struct DenseLayout {
 
 DenseLayout dense_layout(const pararnn_opts* o) {
   DenseLayout y;
-  y.nchunks = (o->L + kDenseChunk - 1) / kDenseChunk;
+  y.nchunks = static_cast<int>(ceil_div(o->L, kDenseChunk));
   const size_t nc = static_cast<size_t>(o->B) * y.nchunks, ns = nc * kDenseWaves;
   y.P = 0;
   y.v = round_up(sizeof(float) * nc * 1024);
@@ -707,6 +720,38 @@ extern "C" int32_t pararnn_solve_gru(const void* u, const float* a, const float*
                static_cast<hipStream_t>(stream));
 }
 
+extern "C" int32_t pararnn_plan_query(int32_t cell, int32_t op, const pararnn_opts* o, pararnn_plan* plan) {
+  if (!plan || !opts_ok(cell, op, o)) return PARARNN_EINVAL;
+  memset(plan, 0, sizeof(*plan));
+  if (op == PARARNN_OP_SCAN_DENSE) {
+    const DenseLayout y = dense_layout(o);
+    plan->vec = 1;
+    plan->chunk = kDenseChunk;
+    plan->channels = o->D;
+    plan->nchunks = y.nchunks;
+    plan->tiles_per_row = o->B;
+    plan->inclusive_only = 1;  // the chunk carries run in order, one workgroup per batch row
+    return PARARNN_OK;
+  }
+  const bool fused = op == PARARNN_OP_SOLVE && use_fused(o);
+  const bool scanop = is_scan(op);
+  const int gcell = scanop ? PARARNN_GRU : cell;  // the scans have no cell
+  const size_t usize = (!scanop && o->u_dtype == PARARNN_BF16) ? 2 : 4;
+  // every pointer 16-byte aligned: the widest channel group that divides D
+  alignas(16) static const char kAligned[16] = {0};
+  const int C = pick_c(cmax_for(gcell, op), o->D, usize, kAligned, {});
+  const Geo g = fused ? fused_geo_for(cell, C) : geo_for(gcell, op, C);
+  const Layout y = layout(gcell, op, o, false, g, fused);
+  plan->vec = C;
+  plan->chunk = g.chunk;
+  plan->channels = g.cw;
+  plan->nchunks = y.nchunks;
+  plan->tiles_per_row = o->B * y.ntiles_d;
+  plan->inclusive_only = incl_only_for(gcell, op, fused, static_cast<long long>(o->B) * y.ntiles_d) ? 1 : 0;
+  plan->fused = fused ? 1 : 0;
+  return PARARNN_OK;
+}
+
 extern "C" size_t pararnn_scratch_bytes(void) { return kScratchBytes; }
 
 extern "C" int32_t pararnn_solve_gru_scratch(const void* u, const float* a, const float* h0, float* h,
@@ -756,7 +801,7 @@ extern "C" int32_t pararnn_adjoint(int32_t cell, const void* u, const float* a, 
 
   int rc = record(o, 0, stream);
   if (rc) return rc;
-  const bool incl_only = static_cast<long long>(o->B) * y.ntiles_d >= iter_incl_tiles(cell);
+  const bool incl_only = incl_only_for(cell, PARARNN_OP_ADJOINT, false, static_cast<long long>(o->B) * y.ntiles_d);
   Layout yc = y;  // inclusive only: the aggregate descriptors are never read
   if (incl_only) yc.zero_end = y.agg;
   rc = clear_ws(w, yc, nullptr, 0, stream);

@@ -69,8 +69,9 @@ WORKLOADS = {
     ]
 }
 
-# The workload the headline throughput number is quoted on.
-HEADLINE = "gru_b8_l4096_d1024_bf16"
+# The workload the headline throughput number is quoted on: the largest one
+# (the 7B-layer-shaped ParaLSTM, forward solve plus adjoint).
+HEADLINE = "lstm_b16_l2048_d4096_bf16_adjoint"
 
 
 @dataclass

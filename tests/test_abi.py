@@ -21,7 +21,8 @@ def test_every_declared_symbol_is_exported(lib):
     names = b.header_functions()
     assert set(names) == {"pararnn_workspace_bytes", "pararnn_solve_gru", "pararnn_solve_lstm",
                           "pararnn_adjoint", "pararnn_scan_diag", "pararnn_scan_block2", "pararnn_scan_dense",
-                          "pararnn_strerror", "pararnn_solve_gru_scratch", "pararnn_scratch_bytes"}
+                          "pararnn_strerror", "pararnn_solve_gru_scratch", "pararnn_scratch_bytes",
+                          "pararnn_plan_query"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -182,3 +183,39 @@ def test_scratch_variant_rejects_before_any_hip_call(lib):
     assert call(2, 8, 4, h=0) == -1
     # the fused B=8 L=4096 D=1024 GRU fits
     assert 0 < _ws(lib, "gru", b.OP_SOLVE, 8, 4096, 1024, 3) <= lib.pararnn_scratch_bytes()
+
+
+def test_plan_query_carry_modes(lib):
+    """The carry mode switches to inclusive only at each kernel family's
+    threshold of workgroups per chunk row (the GPU mode tests rely on these
+    shapes)."""
+    pl = b.plan
+    # fused solve: 32-channel tiles, inclusive only from 64 tiles per row
+    assert pl("gru", b.OP_SOLVE, 1, 700, 2048)["inclusive_only"] == 1
+    assert pl("gru", b.OP_SOLVE, 1, 700, 1024)["inclusive_only"] == 0
+    p = pl("lstm", b.OP_SOLVE, 1, 700, 2048)
+    assert p["inclusive_only"] == 1 and p["fused"] == 1 and p["channels"] == 32
+    # per-iteration schedule: 64-channel tiles; GRU from 128, LSTM from 64 tiles per row
+    assert pl("gru", b.OP_SOLVE, 2, 700, 4096, schedule="per_iteration")["inclusive_only"] == 1
+    assert pl("gru", b.OP_SOLVE, 1, 700, 4096, schedule="per_iteration")["inclusive_only"] == 0
+    assert pl("lstm", b.OP_SOLVE, 1, 700, 4096, schedule="per_iteration")["inclusive_only"] == 1
+    assert pl("lstm", b.OP_SOLVE, 1, 700, 2048, schedule="per_iteration")["inclusive_only"] == 0
+    assert pl("gru", b.OP_SOLVE, 2, 700, 4096, early_exit=True)["fused"] == 0
+    # adjoint: 64-channel tiles; GRU from 128, LSTM from 64
+    assert pl("gru", b.OP_ADJOINT, 2, 700, 4096)["inclusive_only"] == 1
+    assert pl("gru", b.OP_ADJOINT, 1, 700, 4096)["inclusive_only"] == 0
+    assert pl("lstm", b.OP_ADJOINT, 1, 700, 4096)["inclusive_only"] == 1
+    assert pl("lstm", b.OP_ADJOINT, 1, 700, 2048)["inclusive_only"] == 0
+    # scans: from 32 tiles per row (diagonal: 256 channels per tile, 2x2: 128)
+    assert pl("gru", b.OP_SCAN_DIAG, 8, 300, 1024)["inclusive_only"] == 1
+    assert pl("gru", b.OP_SCAN_DIAG, 4, 300, 1024)["inclusive_only"] == 0
+    assert pl("gru", b.OP_SCAN_BLOCK2, 4, 300, 1024)["inclusive_only"] == 1
+    assert pl("gru", b.OP_SCAN_BLOCK2, 2, 300, 1024)["inclusive_only"] == 0
+    # every benchmark workload but the small one runs its look-back kernels inclusive only
+    assert pl("gru", b.OP_SOLVE, 1, 1024, 64, u_dtype=b.F32)["inclusive_only"] == 0
+    for cell, B, L, D in (("gru", 8, 4096, 1024), ("lstm", 8, 4096, 1024), ("gru", 1, 65536, 2048),
+                          ("lstm", 16, 2048, 4096)):
+        assert pl(cell, b.OP_SOLVE, B, L, D)["inclusive_only"] == 1
+    assert pl("lstm", b.OP_ADJOINT, 16, 2048, 4096)["inclusive_only"] == 1
+    with pytest.raises(b.PararnnError):
+        pl("gru", b.OP_SOLVE, 0, 8, 8)

@@ -64,3 +64,45 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode != 0
     msg = json.loads(r.stdout.strip().splitlines()[-1])
     assert msg["n_gpus"] == 2 and "one GPU" in msg["error"]
+
+
+def test_adjoint_traffic_uses_its_own_launches(tmp_path):
+    """The adjoint's bytes come from its own dispatches, not the solve's."""
+    adj = "void pararnn::adjoint_kernel<...>(pararnn::AdjArgs)"
+    fused = "void pararnn::newton_fused_kernel<...>(pararnn::FusedArgs)"
+    f = [(fused, 100.0), (adj, 10.0), (fused, 100.0), (adj, 14.0)]
+    w = [(fused, 50.0), (adj, 4.0), (fused, 50.0), (adj, 6.0)]
+    write_csv(tmp_path / "f.csv", "FETCH_SIZE", calibration(GIB / 2 / 1024) + f)
+    write_csv(tmp_path / "w.csv", "WRITE_SIZE", calibration(GIB / 1024) + w)
+    d = bench.traffic_from_counters("adj_case", str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), 1,
+                                    kernel="adjoint")
+    assert d["per_launch"] == [{"fetch": 12 * 1024 * 2.0, "write": 5 * 1024 * 1.0}]
+    assert d["kernel"] == "adjoint_kernel"
+
+
+def test_valu_slots_from_counters(tmp_path):
+    """Issue slots = 64 lanes x (regular + 4 x transcendental) wave
+    instructions, with the transcendentals taken out of SQ_INSTS_VALU when
+    that counter includes them."""
+    name = "void pararnn::newton_fused_kernel<...>(pararnn::FusedArgs)"
+    with open(tmp_path / "v.csv", "w", newline="") as fh:
+        wr = csv.DictWriter(fh, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        wr.writeheader()
+        for i, (c, v) in enumerate([("SQ_INSTS_VALU", 1000.0), ("SQ_INSTS_VALU_TRANS_F32", 100.0),
+                                    ("SQ_INSTS_VALU", 1200.0), ("SQ_INSTS_VALU_TRANS_F32", 100.0)]):
+            wr.writerow({"Dispatch_Id": i // 2 + 1, "Kernel_Name": name, "Counter_Name": c, "Counter_Value": v})
+    d = bench.valu_from_counters("v_case", str(tmp_path / "v.csv"), elements=64, iters=2, trans_in_valu=True)
+    assert d["per_launch"] == {"SQ_INSTS_VALU": 1100.0, "SQ_INSTS_VALU_TRANS_F32": 100.0}
+    assert d["slots_per_launch"] == 64.0 * (1000.0 + 4 * 100.0)
+    assert d["slots_per_element_iteration"] == 64.0 * 1400.0 / 128
+    d2 = bench.valu_from_counters("v_case", str(tmp_path / "v.csv"), elements=64, iters=2, trans_in_valu=False)
+    assert d2["slots_per_launch"] == 64.0 * (1100.0 + 4 * 100.0)
+
+
+def test_kernel_record_fraction():
+    ms = bench.stats([2.0, 1.0, 3.0])
+    assert ms["mean"] == 2.0 and ms["median"] == 2.0 and ms["min"] == 1.0
+    r = bench.kernel_record("k", "hbm", ms, 8e9, "GB/s", 8000.0)
+    assert abs(r["achieved"] - 4000.0) < 1e-9 and abs(r["frac"] - 0.5) < 1e-12
+    r = bench.kernel_record("k", "alu", ms, None, "T VALU issue slots/s", 78.65)
+    assert r["achieved"] is None and r["frac"] is None
