@@ -35,12 +35,15 @@ from pathlib import Path
 ROOT = Path(__file__).resolve().parent
 PROFILES = ROOT / "profiles"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak
-# Vector-ALU issue peak: the published fp32 vector peak (157.3 TFLOP/s =
-# 256 CUs x 2.4 GHz x 128 FMA lane-slots per clock, 2 flops each) counted in
-# issue slots, one slot per fp32 lane operation.
-PEAK_VALU_TSLOTS = 157.3 / 2.0
-# A transcendental (v_exp_f32, v_rcp_f32) issues at a quarter of the rate.
-TRANS_SLOTS = 4
+# Vector-ALU issue peak for the code this library runs: 256 CUs x 4 SIMDs x
+# 16 lanes x 2.4 GHz = 39.3 T lane operations per second, one issue slot per
+# fp32 lane operation. The published fp32 vector peak (157.3 TFLOP/s) is this
+# rate x 2 flops per FMA x 2 lanes per packed (v_pk_*_f32) instruction; the
+# library is built without packed fp32, so one instruction serves one lane.
+PEAK_VALU_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
+# A transcendental (v_exp_f32, v_rcp_f32) takes two issue slots: the
+# issue-rate kernels measure it at half the FMA rate on this chip.
+TRANS_SLOTS = 2
 PEAK_F32_MATRIX_TFLOPS = 157.3  # MI355X dense fp32 matrix-core peak
 
 
@@ -69,7 +72,7 @@ def adjoint_bytes(cell: str, u_bytes: int) -> int:
 def source_digest() -> str:
     """Digest of the solver's kernel sources with comments and blank lines
     removed, so that counters stay tied to the code they were taken on, not
-    its comments. The measurement probe (issue_rate.hip) is not included."""
+    its comments. The measurement kernels (ceilings.hip) are not included."""
     h = hashlib.sha256()
     csrc = ROOT / "nonlinear_rnn_solve_newton_amd" / "csrc"
     for p in sorted(list(csrc.glob("*.h")) + [csrc / "pararnn.hip"]):
@@ -242,8 +245,22 @@ def write_stats_summary(workload: str, stats_csv: str, command: str) -> str:
 
 
 # ---------------------------------------------------------------------------
-# Same-run device ceilings: a device-to-device copy through torch, and the
-# VALU issue rates of the measurement kernels (issue_rate.hip).
+# Same-run device ceilings: a device-to-device copy through torch, the
+# streaming bandwidth and the VALU issue rates of the measurement kernels
+# (ceilings.hip).
+
+def _ceil_lib():
+    from nonlinear_rnn_solve_newton_amd import build
+
+    if not build.CEIL_LIB.exists():
+        return None
+    L = ctypes.CDLL(str(build.CEIL_LIB))
+    L.ceil_issue_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_float,
+                                    ctypes.c_void_p, ctypes.c_void_p]
+    L.ceil_stream_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_longlong, ctypes.POINTER(ctypes.c_void_p),
+                                     ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    return L
+
 
 def device_ceilings(dev, hip):
     import torch
@@ -265,25 +282,53 @@ def device_ceilings(dev, hip):
     out["device_copy"] = {"gbs": gbs, "frac": gbs / PEAK_HBM_GBS, "bytes": 2 * src.numel() * 4,
                           "what": "torch copy_ of 1 GiB, read + write bytes"}
     del src, dst
-    out["valu_issue"] = issue_rates(dev, hip)
+    L = _ceil_lib()
+    if L is not None:
+        out["streams"] = stream_rates(dev, hip, L)
+        out["valu_issue"] = issue_rates(dev, hip, L)
     return out
 
 
-def issue_rates(dev, hip, waves_per_simd=(1, 2, 3, 8)):
-    """Lane operations per second of the issue-rate kernels, per waves per
-    SIMD (all 256 CUs x 4 SIMDs filled): plain fp32 FMA, v_exp_f32, and the
-    sigmoid-shaped mix, the last in issue slots (transcendentals at
-    TRANS_SLOTS)."""
+def stream_rates(dev, hip, L, n16=1 << 24):
+    """HBM bytes per second of the streaming kernels: 16-byte nontemporal
+    loads and stores over arrays of 256 MiB, read-only, write-only, copy and
+    the adjoint's mix (5 arrays read, 4 written: 20 bytes read per 16
+    written), best of five launches."""
     import torch
 
-    from nonlinear_rnn_solve_newton_amd import build
+    arrays = [torch.ones(n16 * 4, dtype=torch.float32, device=dev) for _ in range(9)]
+    sink = torch.zeros(4, dtype=torch.float32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    ev = hip.create(2)
+    rec = hip.hip.hipEventRecord
+    rec.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    res = {}
+    for name, r, w in (("read", 1, 0), ("write", 0, 1), ("copy", 1, 1), ("read5_write4", 5, 4)):
+        pin = (ctypes.c_void_p * 5)(*[t.data_ptr() for t in arrays[:r]])
+        pout = (ctypes.c_void_p * 4)(*[t.data_ptr() for t in arrays[5:5 + w]])
+        best = None
+        for _ in range(5):
+            rec(ctypes.c_void_p(ev[0]), stream)
+            if L.ceil_stream_launch(r, w, n16, pin, pout, ctypes.c_void_p(sink.data_ptr()), 256 * 32, stream):
+                raise RuntimeError("ceil_stream_launch failed")
+            rec(ctypes.c_void_p(ev[1]), stream)
+            t = hip.ms(ev[0], ev[1])
+            best = t if best is None else min(best, t)
+        gbs = n16 * 16 * (r + w) / (best * 1e-3) / 1e9
+        res[name] = {"gbs": gbs, "frac": gbs / PEAK_HBM_GBS}
+    hip.destroy(ev)
+    del arrays
+    return res
 
-    if not build.ISSUE_LIB.exists():
-        return None
-    L = ctypes.CDLL(str(build.ISSUE_LIB))
-    L.issue_rate_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_float,
-                                    ctypes.c_void_p, ctypes.c_void_p]
-    steps = L.issue_rate_steps_per_trip()
+
+def issue_rates(dev, hip, L, waves_per_simd=(1, 2, 3, 8)):
+    """Lane operations per second of the issue-rate kernels, per waves per
+    SIMD (all 256 CUs x 4 SIMDs filled): plain fp32 FMA, v_exp_f32, and the
+    sigmoid-shaped mix, the last also in issue slots (transcendentals at
+    TRANS_SLOTS) against the issue peak."""
+    import torch
+
+    steps = L.ceil_issue_steps_per_trip()
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     ev = hip.create(2)
     rec = hip.hip.hipEventRecord
@@ -294,20 +339,18 @@ def issue_rates(dev, hip, waves_per_simd=(1, 2, 3, 8)):
         buf = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
         row = {}
         for kind, name, iters, per_step in ((0, "fma", 2000, 1), (1, "exp", 500, 1), (2, "sigmoid_mix", 400, 4)):
-            L.issue_rate_launch(kind, blocks, 10, 0.999, 1e-3, ctypes.c_void_p(buf.data_ptr()), stream)
+            L.ceil_issue_launch(kind, blocks, 10, 0.999, 1e-3, ctypes.c_void_p(buf.data_ptr()), stream)
             rec(ctypes.c_void_p(ev[0]), stream)
-            if L.issue_rate_launch(kind, blocks, iters, 0.999, 1e-3, ctypes.c_void_p(buf.data_ptr()), stream):
-                raise RuntimeError("issue_rate_launch failed")
+            if L.ceil_issue_launch(kind, blocks, iters, 0.999, 1e-3, ctypes.c_void_p(buf.data_ptr()), stream):
+                raise RuntimeError("ceil_issue_launch failed")
             rec(ctypes.c_void_p(ev[1]), stream)
             t = hip.ms(ev[0], ev[1]) * 1e-3
             lane_steps = blocks * 256.0 * iters * steps
+            row[name] = {"lane_ops_per_s": lane_steps * per_step / t,
+                         "per_clock_per_cu_at_2p4GHz": lane_steps * per_step / t / (256 * 2.4e9)}
             if kind == 2:  # 2 regular + 2 transcendental instructions per step
-                row[name] = {"lane_ops_per_s": lane_steps * 4 / t,
-                             "slots_per_s": lane_steps * (2 + 2 * TRANS_SLOTS) / t}
+                row[name]["slots_per_s"] = lane_steps * (2 + 2 * TRANS_SLOTS) / t
                 row[name]["slot_frac_of_peak"] = row[name]["slots_per_s"] / (PEAK_VALU_TSLOTS * 1e12)
-            else:
-                row[name] = {"lane_ops_per_s": lane_steps * per_step / t,
-                             "per_clock_per_cu_at_2p4GHz": lane_steps * per_step / t / (256 * 2.4e9)}
         res[f"{wps}_waves_per_simd"] = row
     hip.destroy(ev)
     return res
@@ -341,12 +384,17 @@ def cpu_baseline(w, x, iters, target_s=15.0, single_s=3.0):
         return len(ch), t1 - t0, t2 - t1, t3 - t2
 
     def scaled(threads, target):
-        n0 = min(BD, max(threads, 16))
-        n, tn, ta, _ = run(n0, threads)
-        per_chan = (tn + ta) / n
-        n = int(min(BD, max(n0, target / max(per_chan, 1e-9))))
-        n = max(threads, n - n % max(threads, 1)) if n < BD else n
-        return run(n, threads)
+        # grow the sample until it takes at least half the target time (or is
+        # the whole workload): a small first sample overstates the per-channel
+        # cost (thread start-up), so one extrapolation falls short
+        n = min(BD, max(threads, 16))
+        while True:
+            res = run(n, threads)
+            t = res[1] + res[2]
+            if n >= BD or t >= 0.5 * target:
+                return res
+            m = int(min(BD, max(2 * n, n * target / max(t, 1e-9))))
+            n = max(threads, m - m % max(threads, 1)) if m < BD else m
 
     n, tn, ta, ts = scaled(nthreads, target_s)
     elems = n * w.L

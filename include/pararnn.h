@@ -106,9 +106,13 @@ typedef struct {
 size_t pararnn_workspace_bytes(int32_t cell, int32_t op, const pararnn_opts* o);
 
 /* ParaGRU forward solve: K Newton iterations from the zero sequence (the
- * initial state h0 is fixed). Iteration k linearises the system at iterate k-1,
- * assembles the diagonal Jacobian coefficients and solves the linear SSM by a
- * parallel scan, in one fused launch. Outputs (device):
+ * initial state h0 is fixed) on the whole-sequence system S_l = f(S_{l-1}, u_l)
+ * (ParaRNN article, cafecomtech.com, section "A sacada: metodo de Newton").
+ * Iteration k linearises the system at iterate k-1, assembles the diagonal
+ * Jacobian coefficients (section "Engenharia pra escalar": diagonal cell
+ * matrices give a diagonal Jacobian) and solves the linear SSM by a parallel
+ * scan (section "O compromisso que SSMs fizeram"); by default all K
+ * iterations run in one fused launch. Outputs (device):
  *   h          [B][L][D] the K-th iterate (always; also with early exit)
  *   iters      [1] number of iterations performed (K unless early exit fired), or NULL
  *   converged  [B] 1 if max |h^(iters) - h^(iters-1)| <= tol on that row, else 0, or NULL
@@ -141,8 +145,10 @@ int32_t pararnn_solve_gru_scratch(const void* u, const float* a, const float* h0
 size_t pararnn_scratch_bytes(void);
 
 /* ParaLSTM forward solve: as pararnn_solve_gru with the 2x2 block Jacobian over
- * (c, h). Outputs c and h, both [B][L][D]; max_update is the max over both
- * state components. */
+ * (c, h) (ParaRNN article, cafecomtech.com, section "Engenharia pra escalar":
+ * diagonal cell matrices give a 2x2 block-diagonal Jacobian for the LSTM;
+ * section "A sacada: metodo de Newton" for the iteration). Outputs c and h,
+ * both [B][L][D]; max_update is the max over both state components. */
 int32_t pararnn_solve_lstm(const void* u, const float* a, const float* c0, const float* h0,
                            float* c, float* h, void* ws, size_t ws_bytes, const pararnn_opts* o,
                            int32_t* iters, int32_t* converged, float* max_update, void* stream);

@@ -17,7 +17,7 @@ PKG = Path(__file__).resolve().parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libpararnn.so"
 # measurement kernels for the device ceilings bench.py reports (not the solver)
-ISSUE_LIB = PKG / "libissuerate.so"
+CEIL_LIB = PKG / "libceilings.so"
 ARCH = "gfx950"
 
 COMMON_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-Wall"]
@@ -49,7 +49,7 @@ def build_one(src: Path, out: Path, verbose: bool = False, extra_flags=(), host_
 
 
 def build(verbose: bool = False, extra_flags=()) -> Path:
-    build_one(CSRC / "issue_rate.hip", ISSUE_LIB, verbose, extra_flags)
+    build_one(CSRC / "ceilings.hip", CEIL_LIB, verbose, extra_flags)
     return build_one(CSRC / "pararnn.hip", LIB, verbose, extra_flags)
 
 

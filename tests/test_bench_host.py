@@ -81,7 +81,7 @@ def test_adjoint_traffic_uses_its_own_launches(tmp_path):
 
 
 def test_valu_slots_from_counters(tmp_path):
-    """Issue slots = 64 lanes x (regular + 4 x transcendental) wave
+    """Issue slots = 64 lanes x (regular + TRANS_SLOTS x transcendental) wave
     instructions, with the transcendentals taken out of SQ_INSTS_VALU when
     that counter includes them."""
     name = "void pararnn::newton_fused_kernel<...>(pararnn::FusedArgs)"
@@ -93,10 +93,11 @@ def test_valu_slots_from_counters(tmp_path):
             wr.writerow({"Dispatch_Id": i // 2 + 1, "Kernel_Name": name, "Counter_Name": c, "Counter_Value": v})
     d = bench.valu_from_counters("v_case", str(tmp_path / "v.csv"), elements=64, iters=2, trans_in_valu=True)
     assert d["per_launch"] == {"SQ_INSTS_VALU": 1100.0, "SQ_INSTS_VALU_TRANS_F32": 100.0}
-    assert d["slots_per_launch"] == 64.0 * (1000.0 + 4 * 100.0)
-    assert d["slots_per_element_iteration"] == 64.0 * 1400.0 / 128
+    T = bench.TRANS_SLOTS
+    assert d["slots_per_launch"] == 64.0 * (1000.0 + T * 100.0)
+    assert d["slots_per_element_iteration"] == 64.0 * (1000.0 + T * 100.0) / 128
     d2 = bench.valu_from_counters("v_case", str(tmp_path / "v.csv"), elements=64, iters=2, trans_in_valu=False)
-    assert d2["slots_per_launch"] == 64.0 * (1100.0 + 4 * 100.0)
+    assert d2["slots_per_launch"] == 64.0 * (1100.0 + T * 100.0)
 
 
 def test_kernel_record_fraction():
