@@ -73,17 +73,21 @@ struct Streams {
   f32x4* out[4];
 };
 
-// R input streams read, W output streams written, n16 16-byte elements each
-template <int R, int W>
+// R input streams read, W output streams written, n16 16-byte elements each;
+// NT: nontemporal loads and stores (else the default cache policy)
+template <int R, int W, bool NT>
 __global__ void __launch_bounds__(256) stream_kernel(const Streams p, long long n16, float* sink) {
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   const long long stride = static_cast<long long>(gridDim.x) * blockDim.x;
   for (long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride) {
     f32x4 v = {1.0f, 2.0f, 3.0f, 4.0f};
 #pragma unroll
-    for (int r = 0; r < R; ++r) v += __builtin_nontemporal_load(p.in[r] + i);
+    for (int r = 0; r < R; ++r) v += NT ? __builtin_nontemporal_load(p.in[r] + i) : p.in[r][i];
 #pragma unroll
-    for (int w = 0; w < W; ++w) __builtin_nontemporal_store(v, p.out[w] + i);
+    for (int w = 0; w < W; ++w) {
+      if constexpr (NT) __builtin_nontemporal_store(v, p.out[w] + i);
+      else p.out[w][i] = v;
+    }
     acc += v;
   }
   if (W == 0 && acc.x == 1234.5f) sink[0] = acc.y;  // keeps the reads of a read-only stream
@@ -93,19 +97,26 @@ __global__ void __launch_bounds__(256) stream_kernel(const Streams p, long long 
 
 // Streams: read `nread` and write `nwrite` device arrays of n16 16-byte
 // elements (in: nread device pointers, out: nwrite device pointers, both host
-// arrays). Supported (nread, nwrite): (1, 0), (0, 1), (1, 1), (5, 4). Returns
-// 0, -1 for a bad argument, -4 when the launch fails.
-extern "C" int ceil_stream_launch(int nread, int nwrite, long long n16, void* const* in, void* const* out,
+// arrays), with nontemporal accesses when nt is 1. Supported (nread, nwrite):
+// (1, 0), (0, 1), (1, 1), (5, 4). Returns 0, -1 for a bad argument, -4 when
+// the launch fails.
+template <bool NT>
+int stream_launch(int nread, int nwrite, long long n16, const Streams& p, float* sink, int blocks, hipStream_t s) {
+  if (nread == 1 && nwrite == 0) hipLaunchKernelGGL((stream_kernel<1, 0, NT>), dim3(blocks), dim3(256), 0, s, p, n16, sink);
+  else if (nread == 0 && nwrite == 1) hipLaunchKernelGGL((stream_kernel<0, 1, NT>), dim3(blocks), dim3(256), 0, s, p, n16, sink);
+  else if (nread == 1 && nwrite == 1) hipLaunchKernelGGL((stream_kernel<1, 1, NT>), dim3(blocks), dim3(256), 0, s, p, n16, sink);
+  else if (nread == 5 && nwrite == 4) hipLaunchKernelGGL((stream_kernel<5, 4, NT>), dim3(blocks), dim3(256), 0, s, p, n16, sink);
+  else return -1;
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+extern "C" int ceil_stream_launch(int nread, int nwrite, int nt, long long n16, void* const* in, void* const* out,
                                   float* sink, int blocks, void* stream) {
   if (n16 < 1 || blocks < 1 || !sink || nread < 0 || nread > 5 || nwrite < 0 || nwrite > 4) return -1;
   Streams p = {};
   for (int r = 0; r < nread; ++r) p.in[r] = static_cast<const f32x4*>(in[r]);
   for (int w = 0; w < nwrite; ++w) p.out[w] = static_cast<f32x4*>(out[w]);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (nread == 1 && nwrite == 0) hipLaunchKernelGGL((stream_kernel<1, 0>), dim3(blocks), dim3(256), 0, s, p, n16, sink);
-  else if (nread == 0 && nwrite == 1) hipLaunchKernelGGL((stream_kernel<0, 1>), dim3(blocks), dim3(256), 0, s, p, n16, sink);
-  else if (nread == 1 && nwrite == 1) hipLaunchKernelGGL((stream_kernel<1, 1>), dim3(blocks), dim3(256), 0, s, p, n16, sink);
-  else if (nread == 5 && nwrite == 4) hipLaunchKernelGGL((stream_kernel<5, 4>), dim3(blocks), dim3(256), 0, s, p, n16, sink);
-  else return -1;
-  return hipGetLastError() == hipSuccess ? 0 : -4;
+  return nt ? stream_launch<true>(nread, nwrite, n16, p, sink, blocks, s)
+            : stream_launch<false>(nread, nwrite, n16, p, sink, blocks, s);
 }

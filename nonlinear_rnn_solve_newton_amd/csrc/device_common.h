@@ -199,7 +199,11 @@ struct URaw<bf16, C> {
 
 // ---------------------------------------------------------------------------
 // Cells. step() evaluates the next state f and its Jacobian J = df/ds at the
-// previous state s. step_adj() returns J and NK coefficients k from which
+// previous state s, J in the cell's compact form Jac. The scan of one Newton
+// iteration, d_l = J_l d_{l-1} + r_l with the residual r_l = f_l - S_l, goes
+// through the cell: residual() forms r in the cell's form, first() and pre()
+// build a lane's composite transform over its steps, apply() takes one step
+// of the recurrence. step_adj() returns J and NK coefficients k from which
 // grad_u() forms, for an adjoint lambda, the input gradient
 // du_g = sum_r lambda_r df_r/du_g and the multiplier m_g of a_g in gate g's
 // pre-activation (dL/da_g = du_g * m_g); k is the compact form of df/du the
@@ -210,46 +214,71 @@ struct GruCell {
   static constexpr int NS = 1;  // state: h
   static constexpr int G = 3;   // gates: z, r, c
 
+  struct Jac {
+    float j;
+  };
+
   // next state and Jacobian from the gate values at state h; Z: h = 0, with
   // the products of the zero state dropped
   template <bool Z>
   __device__ static __forceinline__ void assemble(const float (&a)[G], float z, float r, float c, float h,
-                                                  float (&f)[NS], float (&J)[NS][NS]) {
+                                                  float rh, float (&f)[NS], Jac& J) {
     // J = (1 - z) + z [a_z (1 - z)(c - h) + a_c (1 - c^2) d(rh)/dh], z taken
-    // out of both gate terms (one multiply fewer than summing them). At h = 0
-    // the general form performs the same operations as the zero form:
-    // c - 0 = c and fma(0, x, r) = r.
+    // out of both gate terms (one multiply fewer than summing them), with
+    // d(rh)/dh = r + a_r h r (1 - r) = r + a_r (rh - r rh).
     const float omz = 1.0f - z;
     const float dtc = fmaf(-c, c, 1.0f);  // d tanh / d pre_c
     if constexpr (Z) {
       f[0] = z * c;
-      J[0][0] = fmaf(z, fmaf(a[2], dtc * r, a[0] * (omz * c)), omz);
+      J.j = fmaf(z, fmaf(a[2], dtc * r, a[0] * (omz * c)), omz);
     } else {
       const float cmh = c - h;
       f[0] = fmaf(z, cmh, h);  // (1 - z) h + z c
-      const float drh = fmaf(h * a[1], fmaf(-r, r, r), r);  // d (r h) / dh
-      J[0][0] = fmaf(z, fmaf(a[2], dtc * drh, a[0] * (omz * cmh)), omz);
+      const float drh = fmaf(a[1], fmaf(-r, rh, rh), r);  // d (r h) / dh
+      J.j = fmaf(z, fmaf(a[2], dtc * drh, a[0] * (omz * cmh)), omz);
     }
   }
 
   __device__ static __forceinline__ void step(const float (&a)[G], const float (&u)[G],
-                                              const float (&s)[NS], float (&f)[NS],
-                                              float (&J)[NS][NS]) {
+                                              const float (&s)[NS], float (&f)[NS], Jac& J) {
     const float h = s[0];
     const float z = sigm(fmaf(a[0], h, u[0]));
     const float r = sigm(fmaf(a[1], h, u[1]));
-    const float c = tanh_fast(fmaf(a[2], r * h, u[2]));
-    assemble<false>(a, z, r, c, h, f, J);
+    const float rh = r * h;
+    const float c = tanh_fast(fmaf(a[2], rh, u[2]));
+    assemble<false>(a, z, r, c, h, rh, f, J);
   }
 
   // step() at the zero state h = 0, with the products of the zero state
-  // dropped: equal to step(a, u, {0}) bit for bit when every a is finite
-  // (a * 0 is then a signed zero that the following add absorbs).
+  // dropped: the same values as step(a, u, {0}) when every a is finite (a * 0
+  // is then a signed zero that the following add absorbs).
   __device__ static __forceinline__ void step_zero(const float (&a)[G], const float (&u)[G],
-                                                   float (&f)[NS], float (&J)[NS][NS]) {
-    assemble<true>(a, sigm(u[0]), sigm(u[1]), tanh_fast(u[2]), 0.0f, f, J);
+                                                   float (&f)[NS], Jac& J) {
+    assemble<true>(a, sigm(u[0]), sigm(u[1]), tanh_fast(u[2]), 0.0f, 0.0f, f, J);
   }
 
+  // r = f - S at the step (ZERO: the previous iterate is zero there)
+  template <bool ZERO>
+  __device__ static __forceinline__ void residual(const float (&f)[NS], const float (&so)[NS], const Jac&,
+                                                  float (&r)[NS]) {
+    r[0] = ZERO ? f[0] : f[0] - so[0];
+  }
+  // channel c of a lane's composite transform e: the first step alone, or
+  // the next step composed after it
+  template <class A>
+  __device__ static __forceinline__ void first(A& e, int c, const Jac& J, const float (&r)[NS]) {
+    e.A[0][0][c] = J.j;
+    e.b[0][c] = r[0];
+  }
+  template <class A>
+  __device__ static __forceinline__ void pre(A& e, int c, const Jac& J, const float (&r)[NS]) {
+    e.A[0][0][c] *= J.j;
+    e.b[0][c] = fmaf(J.j, e.b[0][c], r[0]);
+  }
+  // one step of the recurrence: x <- J x + r
+  __device__ static __forceinline__ void apply(const Jac& J, const float (&r)[NS], float (&x)[NS]) {
+    x[0] = fmaf(J.j, x[0], r[0]);
+  }
 
   static constexpr int NK = 4;  // dh'/du_z, dh'/du_r, dh'/du_c, r h
   __device__ static __forceinline__ void step_adj(const float (&a)[G], const float (&u)[G],
@@ -291,35 +320,37 @@ struct LstmCell {
   // multiplier of each gate's pre-activation inside its base-2 exponential
   static constexpr float kScale[G] = {kSigmScale, kSigmScale, kSigmScale, kTanhScale};
 
+  // The 2x2 Jacobian over (c, h) factored as J = [[1, 0], [q, 1]] [[gf, X], [0, w]],
+  // i.e. J = [[gf, X], [q gf, w + q X]]: gf = dc'/dc, X = dc'/dh, q = dh'/dc',
+  // w = dh'/dh through the output gate. With the residual kept as
+  // (r_c, r_h - q r_c), a step of the scan is y_c = gf x_c + X x_h + r_c,
+  // y_h = q y_c + w x_h + (r_h - q r_c): J x + r with fewer operations than
+  // the plain 2x2 form.
+  struct Jac {
+    float gf, X, q, w;
+  };
+
   // next state and Jacobian from the gate values at previous cell state cp;
   // Z: the zero state, with its products dropped
   template <bool Z>
   __device__ static __forceinline__ void assemble(const float (&a)[G], float gi, float gf, float go, float gg,
-                                                  float cp, float (&f)[NS], float (&J)[NS][NS]) {
+                                                  float cp, float (&f)[NS], Jac& J) {
     const float cn = Z ? gi * gg : fmaf(gf, cp, gi * gg);
     const float t = tanh_fast(cn);
+    const float h = go * t;
     f[0] = cn;
-    f[1] = go * t;
-    const float dci = gg * (gi - gi * gi);
-    const float dcg = gi * fmaf(-gg, gg, 1.0f);
-    const float q = go * fmaf(-t, t, 1.0f);  // dh'/dc'
-    const float dho = t * (go - go * go);
-    float X;  // dc'/dh
-    if constexpr (Z) {
-      X = fmaf(dci, a[0], dcg * a[3]);
-    } else {
-      const float dcf = cp * (gf - gf * gf);
-      X = fmaf(dci, a[0], fmaf(dcf, a[1], dcg * a[3]));
-    }
-    J[0][0] = gf;
-    J[0][1] = X;
-    J[1][0] = q * gf;
-    J[1][1] = fmaf(dho, a[2], q * X);
+    f[1] = h;
+    J.gf = gf;
+    J.q = fmaf(-h, t, go);                  // go (1 - t^2)
+    J.w = a[2] * fmaf(-go, h, h);           // a_o t go (1 - go)
+    // X = a_i gg gi (1 - gi) + a_g gi (1 - gg^2) + a_f cp gf (1 - gf); its
+    // first two terms are gi (a_g + gg (a_i - a_i gi - a_g gg))
+    const float bi = fmaf(gg, fmaf(-a[3], gg, fmaf(-a[0], gi, a[0])), a[3]);
+    J.X = Z ? gi * bi : fmaf(a[1] * cp, fmaf(-gf, gf, gf), gi * bi);
   }
 
   __device__ static __forceinline__ void step(const float (&a)[G], const float (&u)[G],
-                                              const float (&s)[NS], float (&f)[NS],
-                                              float (&J)[NS][NS]) {
+                                              const float (&s)[NS], float (&f)[NS], Jac& J) {
     const float hp = s[1];
     assemble<false>(a, sigm(fmaf(a[0], hp, u[0])), sigm(fmaf(a[1], hp, u[1])), sigm(fmaf(a[2], hp, u[2])),
                     tanh_fast(fmaf(a[3], hp, u[3])), s[0], f, J);
@@ -328,21 +359,56 @@ struct LstmCell {
   // step() at the zero state (c, h) = 0, with the products of the zero state
   // dropped: equal to step(a, u, {0, 0}) bit for bit when every a is finite.
   __device__ static __forceinline__ void step_zero(const float (&a)[G], const float (&u)[G],
-                                                   float (&f)[NS], float (&J)[NS][NS]) {
+                                                   float (&f)[NS], Jac& J) {
     assemble<true>(a, sigm(u[0]), sigm(u[1]), sigm(u[2]), tanh_fast(u[3]), 0.0f, f, J);
   }
 
   // step() and step_zero() with the coefficients and inputs already multiplied
   // by kScale (as, us), a keeping the plain coefficients for the Jacobian
   __device__ static __forceinline__ void step_scaled(const float (&a)[G], const float (&as)[G], const float (&us)[G],
-                                                     const float (&s)[NS], float (&f)[NS], float (&J)[NS][NS]) {
+                                                     const float (&s)[NS], float (&f)[NS], Jac& J) {
     const float hp = s[1];
     assemble<false>(a, sigm2(fmaf(as[0], hp, us[0])), sigm2(fmaf(as[1], hp, us[1])),
                     sigm2(fmaf(as[2], hp, us[2])), tanh2(fmaf(as[3], hp, us[3])), s[0], f, J);
   }
   __device__ static __forceinline__ void step_zero_scaled(const float (&a)[G], const float (&us)[G],
-                                                          float (&f)[NS], float (&J)[NS][NS]) {
+                                                          float (&f)[NS], Jac& J) {
     assemble<true>(a, sigm2(us[0]), sigm2(us[1]), sigm2(us[2]), tanh2(us[3]), 0.0f, f, J);
+  }
+
+  // r = (f_c - S_c, (f_h - S_h) - q (f_c - S_c)) at the step (ZERO: the
+  // previous iterate is zero there)
+  template <bool ZERO>
+  __device__ static __forceinline__ void residual(const float (&f)[NS], const float (&so)[NS], const Jac& J,
+                                                  float (&r)[NS]) {
+    r[0] = ZERO ? f[0] : f[0] - so[0];
+    r[1] = fmaf(-J.q, r[0], ZERO ? f[1] : f[1] - so[1]);
+  }
+  template <class A>
+  __device__ static __forceinline__ void first(A& e, int c, const Jac& J, const float (&r)[NS]) {
+    e.A[0][0][c] = J.gf;
+    e.A[0][1][c] = J.X;
+    e.A[1][0][c] = J.q * J.gf;
+    e.A[1][1][c] = fmaf(J.q, J.X, J.w);
+    e.b[0][c] = r[0];
+    e.b[1][c] = fmaf(J.q, r[0], r[1]);
+  }
+  template <class A>
+  __device__ static __forceinline__ void pre(A& e, int c, const Jac& J, const float (&r)[NS]) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const float n0 = fmaf(J.gf, e.A[0][j][c], J.X * e.A[1][j][c]);
+      e.A[1][j][c] = fmaf(J.q, n0, J.w * e.A[1][j][c]);
+      e.A[0][j][c] = n0;
+    }
+    const float b0 = fmaf(J.gf, e.b[0][c], fmaf(J.X, e.b[1][c], r[0]));
+    e.b[1][c] = fmaf(J.q, b0, fmaf(J.w, e.b[1][c], r[1]));
+    e.b[0][c] = b0;
+  }
+  __device__ static __forceinline__ void apply(const Jac& J, const float (&r)[NS], float (&x)[NS]) {
+    const float y0 = fmaf(J.gf, x[0], fmaf(J.X, x[1], r[0]));
+    x[1] = fmaf(J.q, y0, fmaf(J.w, x[1], r[1]));
+    x[0] = y0;
   }
 
   // q = dh'/dc', then dc'/du_i, dc'/du_f, dc'/du_g and dh'/du_o; the input

@@ -199,9 +199,9 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_fused_kernel(const FusedAr
     unsigned long long* incl = p.incl + (k - 1) * inc_k;
     [[maybe_unused]] unsigned long long* agg = p.agg + (k - 1) * agg_k;
     unsigned long long early[NS][C];  // the predecessor's inclusive carry, read early
-    float Jt[T][NS][NS][C], rt[T][NS][C];
-    Aff<NS, C> acc;
-    acc.set_identity();
+    typename Cell::Jac Jt[T][C];
+    float rt[T][NS][C];
+    Aff<NS, C> acc;  // the lane's transform over its steps, from its first step
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       if (t == TPOLL) {
@@ -231,11 +231,15 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_fused_kernel(const FusedAr
       }
 #pragma unroll
       for (int c = 0; c < C; ++c) {
-        float ac[G], uc[G], pc[NS], f[NS], J[NS][NS];
+        float ac[G], uc[G], pc[NS], f[NS], sc[NS], rr[NS];
+        typename Cell::Jac J;
 #pragma unroll
         for (int g = 0; g < G; ++g) { ac[g] = av[g][c]; uc[g] = UMODE == 3 ? uts[g][c] : ut[g].get(c); }
 #pragma unroll
-        for (int s = 0; s < NS; ++s) pc[s] = (t == 0) ? sp[s][c] : so[t - 1][s][c];
+        for (int s = 0; s < NS; ++s) {
+          pc[s] = (t == 0) ? sp[s][c] : so[t - 1][s][c];
+          sc[s] = so[t][s][c];
+        }
         if constexpr (UMODE == 3) {
           float acs[G];
 #pragma unroll
@@ -246,14 +250,13 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_fused_kernel(const FusedAr
           if (ZERO && t > 1) Cell::step_zero(ac, uc, f, J);
           else Cell::step(ac, uc, pc, f, J);
         }
+        Cell::template residual<ZERO>(f, sc, J, rr);
+        Jt[t][c] = J;
 #pragma unroll
-        for (int r = 0; r < NS; ++r) {
-#pragma unroll
-          for (int s = 0; s < NS; ++s) Jt[t][r][s][c] = J[r][s];
-          rt[t][r][c] = ZERO ? f[r] : f[r] - so[t][r][c];
-        }
+        for (int r = 0; r < NS; ++r) rt[t][r][c] = rr[r];
+        if (t == 0) Cell::first(acc, c, J, rr);
+        else Cell::pre(acc, c, J, rr);
       }
-      acc.pre(Jt[t], rt[t]);
     }
 
     Aff<NS, C> excl;
@@ -355,16 +358,19 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_fused_kernel(const FusedAr
     float mx = 0.0f;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      float y[NS][C];
+      float y[NS][C];  // the update d at the step: J d_prev + r
 #pragma unroll
-      for (int c = 0; c < C; ++c)
+      for (int c = 0; c < C; ++c) {
+        float xs[NS], rr[NS];
 #pragma unroll
         for (int r = 0; r < NS; ++r) {
-          float a2 = rt[t][r][c];
-#pragma unroll
-          for (int s = 0; s < NS; ++s) a2 = fmaf(Jt[t][r][s][c], x[s][c], a2);
-          y[r][c] = a2;
+          xs[r] = x[r][c];
+          rr[r] = rt[t][r][c];
         }
+        Cell::apply(Jt[t][c], rr, xs);
+#pragma unroll
+        for (int r = 0; r < NS; ++r) y[r][c] = xs[r];
+      }
       const bool valid = FULL || (dv && l0 + t < p.L);
 #pragma unroll
       for (int r = 0; r < NS; ++r)

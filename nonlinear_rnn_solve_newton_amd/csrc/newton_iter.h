@@ -294,18 +294,22 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_iter_kernel(const IterArgs
   }
 
   // ---- a2 + a3: residual and Jacobian per step; serial scan of the lane's T steps
-  float Jt[T][NS][NS][C], rt[T][NS][C];
-  Aff<NS, C> acc;
-  acc.set_identity();
+  typename Cell::Jac Jt[T][C];
+  float rt[T][NS][C];
+  Aff<NS, C> acc;  // the lane's transform over its steps, from its first step
 #pragma unroll
   for (int t = 0; t < T; ++t) {
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-      float ac[G], uc[G], pc[NS], f[NS], J[NS][NS];
+      float ac[G], uc[G], pc[NS], f[NS], sc[NS], rr[NS];
+      typename Cell::Jac J;
 #pragma unroll
       for (int g = 0; g < G; ++g) { ac[g] = av[g][c]; uc[g] = uu[t][g].get(c); }
 #pragma unroll
-      for (int s = 0; s < NS; ++s) pc[s] = (t == 0) ? sp[s][c] : so[t - 1][s][c];
+      for (int s = 0; s < NS; ++s) {
+        pc[s] = (t == 0) ? sp[s][c] : so[t - 1][s][c];
+        sc[s] = so[t][s][c];
+      }
       // Iteration 1 linearises at the zero iterate: from the third step of a
       // lane on the cell is evaluated in its reduced form at the zero state.
       // The general form on the first two steps (the second of the sequence's
@@ -314,14 +318,13 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_iter_kernel(const IterArgs
       // (inf * 0 = NaN enters r_t, and the scan carries it to every later step).
       if (FIRST && t > 1) Cell::step_zero(ac, uc, f, J);
       else Cell::step(ac, uc, pc, f, J);
+      Cell::template residual<FIRST>(f, sc, J, rr);
+      Jt[t][c] = J;
 #pragma unroll
-      for (int r = 0; r < NS; ++r) {
-#pragma unroll
-        for (int s = 0; s < NS; ++s) Jt[t][r][s][c] = J[r][s];
-        rt[t][r][c] = f[r] - so[t][r][c];
-      }
+      for (int r = 0; r < NS; ++r) rt[t][r][c] = rr[r];
+      if (t == 0) Cell::first(acc, c, J, rr);
+      else Cell::pre(acc, c, J, rr);
     }
-    acc.pre(Jt[t], rt[t]);
   }
 
   // ---- a4: scan across the LL lane groups of the wave (shuffles) -----------
@@ -423,20 +426,18 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_iter_kernel(const IterArgs
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     const int l = l0 + t;
-    float y[NS][C];
 #pragma unroll
-    for (int c = 0; c < C; ++c)
+    for (int c = 0; c < C; ++c) {
+      float xs[NS], rr[NS];
 #pragma unroll
       for (int r = 0; r < NS; ++r) {
-        float acc2 = rt[t][r][c];
-#pragma unroll
-        for (int s = 0; s < NS; ++s) acc2 = fmaf(Jt[t][r][s][c], x[s][c], acc2);
-        y[r][c] = acc2;
+        xs[r] = x[r][c];
+        rr[r] = rt[t][r][c];
       }
+      Cell::apply(Jt[t][c], rr, xs);
 #pragma unroll
-    for (int r = 0; r < NS; ++r)
-#pragma unroll
-      for (int c = 0; c < C; ++c) x[r][c] = y[r][c];
+      for (int r = 0; r < NS; ++r) x[r][c] = xs[r];
+    }
     const bool valid = FULL || (dv && l < p.L);
 #pragma unroll
     for (int r = 0; r < NS; ++r) {
