@@ -257,7 +257,7 @@ def _ceil_lib():
     L = ctypes.CDLL(str(build.CEIL_LIB))
     L.ceil_issue_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_float,
                                     ctypes.c_void_p, ctypes.c_void_p]
-    L.ceil_stream_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_longlong, ctypes.POINTER(ctypes.c_void_p),
+    L.ceil_stream_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_longlong, ctypes.POINTER(ctypes.c_void_p),
                                      ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     return L
 
@@ -290,10 +290,10 @@ def device_ceilings(dev, hip):
 
 
 def stream_rates(dev, hip, L, n16=1 << 24):
-    """HBM bytes per second of the streaming kernels: 16-byte nontemporal
-    loads and stores over arrays of 256 MiB, read-only, write-only, copy and
-    the adjoint's mix (5 arrays read, 4 written: 20 bytes read per 16
-    written), best of five launches."""
+    """HBM bytes per second of the streaming kernels: 16-byte loads and
+    stores over arrays of 256 MiB, read-only, write-only, copy and the
+    adjoint's mix (5 arrays read, 4 written: 20 bytes read per 16 written),
+    with nontemporal and with default-policy accesses, best of five launches."""
     import torch
 
     arrays = [torch.ones(n16 * 4, dtype=torch.float32, device=dev) for _ in range(9)]
@@ -303,13 +303,15 @@ def stream_rates(dev, hip, L, n16=1 << 24):
     rec = hip.hip.hipEventRecord
     rec.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     res = {}
-    for name, r, w in (("read", 1, 0), ("write", 0, 1), ("copy", 1, 1), ("read5_write4", 5, 4)):
+    for name, r, w, nt in [(f"{n}{'_nt' if nt else ''}", r, w, nt) for n, r, w in
+                           (("read", 1, 0), ("write", 0, 1), ("copy", 1, 1), ("read5_write4", 5, 4))
+                           for nt in (1, 0)]:
         pin = (ctypes.c_void_p * 5)(*[t.data_ptr() for t in arrays[:r]])
         pout = (ctypes.c_void_p * 4)(*[t.data_ptr() for t in arrays[5:5 + w]])
         best = None
         for _ in range(5):
             rec(ctypes.c_void_p(ev[0]), stream)
-            if L.ceil_stream_launch(r, w, n16, pin, pout, ctypes.c_void_p(sink.data_ptr()), 256 * 32, stream):
+            if L.ceil_stream_launch(r, w, nt, n16, pin, pout, ctypes.c_void_p(sink.data_ptr()), 256 * 32, stream):
                 raise RuntimeError("ceil_stream_launch failed")
             rec(ctypes.c_void_p(ev[1]), stream)
             t = hip.ms(ev[0], ev[1])
@@ -662,19 +664,27 @@ def bench_solve(w, args):
                 binding.adjoint(w.cell, u, a, out["h"], dh, c=out.get("c"), ws=gadj["ws"], du=gadj["du"],
                                 events=events_adj)
 
+        def kernel_times():
+            launch_ms = [[] for _ in range(K)]
+            clear_ms, adj_ms = [], []
+            for _ in range(args.steps):
+                step(ev, ev_adj)
+                # event 1: the first launch's start; k + 1: the end of
+                # iteration k's launch (for the fused schedule its one launch,
+                # then markers right after it)
+                clear_ms.append(hip.ms(ev[0], ev[1]))
+                for k in range(K):
+                    launch_ms[k].append(hip.ms(ev[k + 1], ev[k + 2]))
+                if w.adjoint:
+                    adj_ms.append(hip.ms(ev_adj[1], ev_adj[2]))
+            return launch_ms, clear_ms, adj_ms
+
+        # the per-kernel timing runs once before the timed steps, which lets
+        # the clocks settle under this load (its figures are not used), and
+        # once after them for the reported kernel durations
+        kernel_times()
         ms_step, step_stats = timed_steps(step, args.steps, args.warmup)
-        launch_ms = [[] for _ in range(K)]
-        clear_ms, adj_ms = [], []
-        for _ in range(args.steps):
-            step(ev, ev_adj)
-            # event 1: the first launch's start; k + 1: the end of iteration
-            # k's launch (for the fused schedule its one launch, then markers
-            # right after it)
-            clear_ms.append(hip.ms(ev[0], ev[1]))
-            for k in range(K):
-                launch_ms[k].append(hip.ms(ev[k + 1], ev[k + 2]))
-            if w.adjoint:
-                adj_ms.append(hip.ms(ev_adj[1], ev_adj[2]))
+        launch_ms, clear_ms, adj_ms = kernel_times()
         return {"ms_step": ms_step, "step": step_stats, "clear_ms": stats(clear_ms),
                 "launch_ms": [stats(v) for v in launch_ms], "adj_ms": stats(adj_ms) if adj_ms else None,
                 "out": out, "gadj": gadj}
