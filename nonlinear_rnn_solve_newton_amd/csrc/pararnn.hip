@@ -32,7 +32,7 @@ template <> struct Cfg<GruCell, 1, false> { static constexpr int T = 32, W = 4, 
 template <> struct Cfg<LstmCell, 1, false> { static constexpr int T = 24, W = 4, LL = 1, OCC = 2; };
 template <> struct Cfg<GruCell, 2, true> { static constexpr int T = 8, W = 4, LL = 2, OCC = 2; };
 template <> struct Cfg<GruCell, 1, true> { static constexpr int T = 8, W = 8, LL = 2, OCC = 2; };
-template <> struct Cfg<LstmCell, 1, true> { static constexpr int T = 16, W = 4, LL = 1, OCC = 2; };
+template <> struct Cfg<LstmCell, 1, true> { static constexpr int T = 9, W = 4, LL = 1, OCC = 3; };
 // All K iterations in one launch (newton_fused.h): the iterate stays in
 // registers between iterations; UMODE says where the gate inputs stay (1:
 // registers, 2: workgroup memory as read, 3: workgroup memory widened and
