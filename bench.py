@@ -207,15 +207,21 @@ def valu_from_counters(workload: str, csv_path: str, elements: int, iters: int, 
                        kernel: str = "newton_fused") -> dict:
     """VALU issue slots per launch of one kernel from a rocprofv3 --pmc run with
     SQ_INSTS_VALU and SQ_INSTS_VALU_TRANS_F32 (wave instructions per
-    dispatch): lane slots = 64 x (regular + TRANS_SLOTS x transcendental).
+    dispatch): lane slots = 64 x (regular + TRANS_SLOTS x transcendental). The
+    per-launch means of every other SQ counter of the pass are kept too.
     trans_in_valu says whether SQ_INSTS_VALU already counts the
     transcendentals (measured with the issue-rate probe's exp-only kernel)."""
+    import csv
+
+    names = sorted({r["Counter_Name"] for r in csv.DictReader(open(csv_path))})
     per = {}
-    for c in VALU_COUNTERS:
+    for c in names:
         vals = [float(r["Counter_Value"]) for r in _counter_rows(csv_path, c) if f"{kernel}_kernel" in r["Kernel_Name"]]
-        if not vals:
+        if vals:
+            per[c] = sum(vals) / len(vals)
+    for c in VALU_COUNTERS:
+        if c not in per:
             raise ValueError(f"no {c} rows for {kernel}_kernel in {csv_path}")
-        per[c] = sum(vals) / len(vals)
     trans = per["SQ_INSTS_VALU_TRANS_F32"]
     regular = per["SQ_INSTS_VALU"] - (trans if trans_in_valu else 0.0)
     slots = 64.0 * (regular + TRANS_SLOTS * trans)
@@ -815,9 +821,11 @@ def main(argv=None):
         return 0
     if args.valu_from:
         w = WORKLOADS[name]
-        d = valu_from_counters(name, args.valu_from, w.N, w.iters, args.trans_in_valu == "yes")
-        valu_path(name).write_text(json.dumps(d, indent=1) + "\n")
-        print(json.dumps(d))
+        kernels = [("newton_fused", w.iters)] + ([("adjoint", 1)] if w.adjoint else [])
+        for kern, iters in kernels:
+            d = valu_from_counters(name, args.valu_from, w.N, iters, args.trans_in_valu == "yes", kernel=kern)
+            valu_path(name, kern).write_text(json.dumps(d, indent=1) + "\n")
+            print(json.dumps(d))
         return 0
     if args.traffic_from:
         if name in SCAN_WORKLOADS:
