@@ -7,11 +7,16 @@
 //   J_{l+1} = df/ds(S_l, u_{l+1}),  G_l = dh_l on the h component,
 //   du_l = (df/du(S_{l-1}, u_l))^T lambda_l,  ds0 = J_0^T lambda_0,
 //   da_g = sum_{b,l} m_g(S_{l-1}) du_{l,g}   (m_g: multiplier of a_g in gate g).
-// The recurrence for lambda is again a linear SSM (with the transposed
-// Jacobians, run from the end of the sequence), so it uses the same scan
-// hierarchy as the Newton iteration with the direction reversed: lanes,
-// waves and chunks are ordered from the end of L, and the look-back walks to
-// larger chunk indices. The ParaRNN pages state that training runs in
+// The scan runs on mu_l = J_l^T lambda_l, the gradient that step l passes
+// back to S_{l-1}:
+//   mu_L = 0,  lambda_l = mu_{l+1} + G_l,  mu_l = J_l^T lambda_l,  ds0 = mu_0,
+// a linear SSM again (with the transposed Jacobians, run from the end of the
+// sequence) in which step l needs only its own Jacobian, at (S_{l-1}, u_l).
+// A lane that owns steps l0 .. l0+T-1 so reads exactly the rows it owns of u
+// and dh, and the rows l0-1 .. l0+T-2 of S: the lanes tile every array
+// without overlap. It uses the same scan hierarchy as the Newton iteration
+// with the direction reversed: lanes, waves and chunks are ordered from the
+// end of L, and the look-back walks to larger chunk indices. The ParaRNN pages state that training runs in
 // parallel (cafecomtech.com article, opening; aifeed.sk article); the adjoint
 // is the standard reverse-mode form of the recurrence.
 #pragma once
@@ -71,9 +76,8 @@ __global__ void __launch_bounds__(64 * W, OCC) adjoint_kernel(const AdjArgs p) {
   const long long BD = static_cast<long long>(p.B) * p.ntiles_d * CW;  // descriptor slots per component
   const long long chan = static_cast<long long>(tile) * CW + ld;
   // Addressing as in the Newton iteration: per-chunk buffer resources over
-  // batch row b (u one row past the chunk, for the Jacobian of the step that
-  // follows the chunk), 32-bit lane offsets, rows at or past L read 0 and
-  // drop stores, lanes past D get an offset beyond every extent.
+  // batch row b, 32-bit lane offsets, rows at or past L read 0 and drop
+  // stores, lanes past D get an offset beyond every extent.
   const long long wrow = static_cast<long long>(b) * p.L + static_cast<long long>(chunk) * CL;
   const uint32_t ustep = static_cast<uint32_t>(G * p.D * sizeof(UT));
   const uint32_t gstep = static_cast<uint32_t>(p.D * sizeof(UT));
@@ -81,13 +85,12 @@ __global__ void __launch_bounds__(64 * W, OCC) adjoint_kernel(const AdjArgs p) {
   const uint32_t dstep = static_cast<uint32_t>(G * p.D * sizeof(float));
   const int crow = p.L - chunk * CL;  // rows from the chunk start to the end of L
   const uint32_t rows = static_cast<uint32_t>(min(crow, CL));
-  const uint32_t rows_u = static_cast<uint32_t>(min(crow, CL + 1));
   constexpr uint32_t kOOB = 0x80000000u;  // extents stay below 2^31 bytes
   const uint32_t vu0 = dv ? static_cast<uint32_t>(lt0) * ustep + static_cast<uint32_t>(d0 * sizeof(UT)) : kOOB;
   const uint32_t vs0 = dv ? static_cast<uint32_t>(lt0) * sstep + static_cast<uint32_t>(d0 * sizeof(float)) : kOOB;
   const uint32_t vd0 = dv ? static_cast<uint32_t>(lt0) * dstep + static_cast<uint32_t>(d0 * sizeof(float)) : kOOB;
   const __amdgpu_buffer_rsrc_t ru =
-      make_rsrc(reinterpret_cast<const char*>(p.u) + wrow * G * p.D * static_cast<long long>(sizeof(UT)), rows_u * ustep);
+      make_rsrc(reinterpret_cast<const char*>(p.u) + wrow * G * p.D * static_cast<long long>(sizeof(UT)), rows * ustep);
   __amdgpu_buffer_rsrc_t rS[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) rS[s] = make_rsrc(p.S[s] + wrow * p.D, rows * sstep);
@@ -100,20 +103,20 @@ __global__ void __launch_bounds__(64 * W, OCC) adjoint_kernel(const AdjArgs p) {
 #pragma unroll
     for (int c = 0; c < C; ++c) dacc[g][c] = 0.0f;
 
-  // The tile body, instantiated for tiles whose steps (including the one after
-  // the chunk) all lie below L and whose channels all lie below D, and for
-  // the others, which mask the steps past L to identity transforms.
+  // The tile body, instantiated for tiles whose steps all lie below L and
+  // whose channels all lie below D, and for the others, which mask the steps
+  // past L to identity transforms.
   auto tile_body = [&](auto full_tag) {
   constexpr bool FULL = decltype(full_tag)::value;
   const int dc = dv ? d0 : p.D - C;  // channel group for the per-channel loads
   float av[G][C];
 #pragma unroll
   for (int g = 0; g < G; ++g) ld_f32<C>(p.a + static_cast<long long>(g) * p.D + dc, av[g]);
-  // states S_{m-1} and inputs u_m for m = l0 .. l0 + T; S_{l0-1} is the
-  // initial state at l0 == 0 and otherwise the row before the lane (clamped
-  // into the sequence for lanes past L, whose steps are masked)
-  float sv[T + 1][NS][C];
-  URaw<UT, C> uu[T + 1][G];
+  // states S_{m-1}, inputs u_m and dh_m for m = l0 .. l0 + T - 1; S_{l0-1} is
+  // the initial state at l0 == 0 and otherwise the row before the lane
+  // (clamped into the sequence for lanes past L, whose steps are masked)
+  float sv[T][NS][C];
+  URaw<UT, C> uu[T][G];
   float gv[T][C];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
@@ -127,23 +130,22 @@ __global__ void __launch_bounds__(64 * W, OCC) adjoint_kernel(const AdjArgs p) {
     for (int c = 0; c < C; ++c) sv[0][s][c] = (l0 == 0) ? v0[c] : v1[c];
   }
 #pragma unroll
-  for (int t = 0; t <= T; ++t) {
+  for (int t = 0; t < T; ++t) {
     if (t > 0) {
 #pragma unroll
       for (int s = 0; s < NS; ++s) buf_ld_f32<C>(rS[s], vs0 + (t - 1) * sstep, 0u, sv[t][s]);
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) uu[t][g].load(ru, vu0 + t * ustep, static_cast<uint32_t>(g) * gstep);
-    if (t < T) buf_ld_f32<C>(rdh, vs0 + t * sstep, 0u, gv[t]);
+    buf_ld_f32<C>(rdh, vs0 + t * sstep, 0u, gv[t]);
   }
 
-  // cell evaluations at m = l0 + t: J_m for t = 0..T, the input-gradient
-  // coefficients for t < T
+  // cell evaluations at m = l0 + t: J_m and the input-gradient coefficients
   constexpr int NK = Cell::NK;
-  float Jm[T + 1][NS][NS][C];
+  float Jm[T][NS][NS][C];
   float kc[T][NK][C];
 #pragma unroll
-  for (int t = 0; t <= T; ++t) {
+  for (int t = 0; t < T; ++t) {
     const bool v = FULL || (dv && (l0 + t) < p.L);
 #pragma unroll
     for (int c = 0; c < C; ++c) {
@@ -157,14 +159,13 @@ __global__ void __launch_bounds__(64 * W, OCC) adjoint_kernel(const AdjArgs p) {
       for (int r = 0; r < NS; ++r)
 #pragma unroll
         for (int s = 0; s < NS; ++s) Jm[t][r][s][c] = v ? J[r][s] : (r == s ? 1.0f : 0.0f);
-      if (t < T) {
 #pragma unroll
-        for (int i = 0; i < NK; ++i) kc[t][i][c] = kk[i];
-      }
+      for (int i = 0; i < NK; ++i) kc[t][i][c] = kk[i];
     }
   }
 
-  // serial reverse scan over the lane's steps: lambda_l = J_{l+1}^T lambda_{l+1} + G_l
+  // serial reverse scan over the lane's steps: mu_l = J_l^T (mu_{l+1} + G_l)
+  // (masked steps: identity, and dh reads 0 past L)
   Aff<NS, C> acc;
   acc.set_identity();
 #pragma unroll
@@ -175,8 +176,8 @@ __global__ void __launch_bounds__(64 * W, OCC) adjoint_kernel(const AdjArgs p) {
 #pragma unroll
       for (int c = 0; c < C; ++c) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) e.A[r][s][c] = Jm[t + 1][s][r][c];  // transpose
-        e.b[r][c] = (r == NS - 1) ? gv[t][c] : 0.0f;
+        for (int s = 0; s < NS; ++s) e.A[r][s][c] = Jm[t][s][r][c];  // transpose
+        e.b[r][c] = Jm[t][NS - 1][r][c] * gv[t][c];  // J^T G, G on the h component
       }
     e.after(acc);
     acc = e;
@@ -253,11 +254,11 @@ __global__ void __launch_bounds__(64 * W, OCC) adjoint_kernel(const AdjArgs p) {
   }
   __syncthreads();
 
-  float lam[NS][C];
+  float mu[NS][C];  // mu at the row after the lane's last step
 #pragma unroll
   for (int s = 0; s < NS; ++s)
 #pragma unroll
-    for (int c = 0; c < C; ++c) lam[s][c] = s_carry[s][ld * C + c];
+    for (int c = 0; c < C; ++c) mu[s][c] = s_carry[s][ld * C + c];
   for (int w = 0; w < wave; ++w) {
     Aff<NS, C> e;
 #pragma unroll
@@ -268,27 +269,18 @@ __global__ void __launch_bounds__(64 * W, OCC) adjoint_kernel(const AdjArgs p) {
         for (int s = 0; s < NS; ++s) e.A[r][s][c] = s_agg[w][r * NS + s][ld * C + c];
         e.b[r][c] = s_agg[w][NS * NS + r][ld * C + c];
       }
-    e.apply(lam);
+    e.apply(mu);
   }
-  if constexpr (LL > 1) excl.apply(lam);
+  if constexpr (LL > 1) excl.apply(mu);
 
 #pragma unroll
   for (int t = T - 1; t >= 0; --t) {
     const int l = l0 + t;
-    float y[NS][C];
-#pragma unroll
-    for (int c = 0; c < C; ++c)
-#pragma unroll
-      for (int r = 0; r < NS; ++r) {
-        float a2 = (r == NS - 1) ? gv[t][c] : 0.0f;
-#pragma unroll
-        for (int s = 0; s < NS; ++s) a2 = fmaf(Jm[t + 1][s][r][c], lam[s][c], a2);
-        y[r][c] = a2;
-      }
+    float lam[NS][C];  // lambda_l = mu_{l+1} + G_l
 #pragma unroll
     for (int r = 0; r < NS; ++r)
 #pragma unroll
-      for (int c = 0; c < C; ++c) lam[r][c] = y[r][c];
+      for (int c = 0; c < C; ++c) lam[r][c] = (r == NS - 1) ? mu[r][c] + gv[t][c] : mu[r][c];
     const bool valid = FULL || (dv && l < p.L);
     float o[G][C];
 #pragma unroll
@@ -308,23 +300,23 @@ __global__ void __launch_bounds__(64 * W, OCC) adjoint_kernel(const AdjArgs p) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
       buf_st_f32<C, kBufNT>(rdu, vd0 + t * dstep, static_cast<uint32_t>(g) * sstep, o[g]);  // dropped past L or D
-    if (l == 0 && dv && p.ds0) {
+    // mu_l = J_l^T lambda_l
+#pragma unroll
+    for (int c = 0; c < C; ++c)
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        float o[C];
+        float a2 = 0.0f;
 #pragma unroll
-        for (int c = 0; c < C; ++c) {
-          float a2 = 0.0f;
-#pragma unroll
-          for (int r = 0; r < NS; ++r) a2 = fmaf(Jm[0][r][s][c], lam[r][c], a2);
-          o[c] = a2;
-        }
-        st_f32<C>(p.ds0 + (static_cast<long long>(s) * p.B + b) * p.D + d0, o);
+        for (int r = 0; r < NS; ++r) a2 = fmaf(Jm[t][r][s][c], lam[r][c], a2);
+        mu[s][c] = a2;
       }
+    if (l == 0 && dv && p.ds0) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) st_f32<C>(p.ds0 + (static_cast<long long>(s) * p.B + b) * p.D + d0, mu[s]);
     }
   }
   };
-  const bool full = (chunk + 1) * CL < p.L && dt0 + CW <= p.D;
+  const bool full = (chunk + 1) * CL <= p.L && dt0 + CW <= p.D;
   if (full) tile_body(std::true_type{});
   else tile_body(std::false_type{});
 
