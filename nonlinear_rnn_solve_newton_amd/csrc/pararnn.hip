@@ -791,9 +791,8 @@ extern "C" int32_t pararnn_adjoint(int32_t cell, const void* u, const float* a, 
                       {a, h0, h, dh, du, ds0, da, lstm ? c0 : nullptr, lstm ? c : nullptr});
   if (!C || !aligned(u, usize)) return PARARNN_EUNSUPPORTED;
   const Geo g = geo_for(cell, PARARNN_OP_ADJOINT, C);
-  // one chunk of gate inputs (plus the row after it) and of du is addressed
-  // with 32-bit offsets below 2^31
-  if ((g.chunk + 1.0) * ngates(cell) * o->D * 4.0 >= 2147483648.0) return PARARNN_EUNSUPPORTED;
+  // one chunk of gate inputs and of du is addressed with 32-bit offsets below 2^31
+  if (static_cast<double>(g.chunk) * ngates(cell) * o->D * 4.0 >= 2147483648.0) return PARARNN_EUNSUPPORTED;
   const Layout y = layout(cell, PARARNN_OP_ADJOINT, o, da != nullptr, g);
   if (ws_bytes < y.total) return PARARNN_EWORKSPACE;
   if (!aligned(ws, kAlign)) return PARARNN_EUNSUPPORTED;

@@ -104,6 +104,27 @@ int main() {
                     : pararnn_scan_dense(nullptr, (float*)fake(2), nullptr, (float*)fake(3), fake(4), 0, &so, nullptr);
     CHECK(rc == PARARNN_EINVAL, "scan %d NULL A", which);
   }
+  // the largest channel count whose chunk of gate inputs (and of du) stays
+  // below 2^31 bytes is accepted (the zero-byte workspace is then the first
+  // refusal), the next one is not: LSTM solve under both schedules, adjoint
+  for (int op = 0; op <= 1; ++op)
+    for (int sch = 1; sch <= (op == 0 ? 2 : 1); ++sch) {
+      pararnn_opts lo = opts(1, 64, 1024, 3, 1, sch, 0);
+      pararnn_plan p;
+      CHECK(pararnn_plan_query(1, op, &lo, &p) == 0, "plan op %d schedule %d", op, sch);
+      const long long per = static_cast<long long>(p.chunk) * 4 * 4;  // bytes of one channel's chunk: 4 gates, fp32
+      const int dmax = static_cast<int>((2147483648LL + per - 1) / per - 1);
+      for (int D : {dmax, dmax + 1}) {
+        lo.D = D;
+        const int rc = op == 0 ? pararnn_solve_lstm(fake(1), (float*)fake(2), nullptr, nullptr, (float*)fake(5),
+                                                    (float*)fake(3), fake(4), 0, &lo, nullptr, nullptr, nullptr, nullptr)
+                               : pararnn_adjoint(1, fake(1), (float*)fake(2), nullptr, nullptr, (float*)fake(5),
+                                                 (float*)fake(3), (float*)fake(6), (float*)fake(7), nullptr, nullptr,
+                                                 fake(4), 0, &lo, nullptr);
+        CHECK(rc == (D == dmax ? PARARNN_EWORKSPACE : PARARNN_EUNSUPPORTED), "extent limit op %d schedule %d D %d: %d",
+              op, sch, D, rc);
+      }
+    }
   const pararnn_opts big = opts(8, 4096, 1024, 3, 1, 2, 0);  // per-iteration state buffer beyond the scratch
   CHECK(pararnn_solve_gru_scratch(fake(1), (float*)fake(2), nullptr, (float*)fake(3), &big, nullptr, nullptr,
                                   nullptr, nullptr) == PARARNN_ESCRATCH, "scratch too small");
