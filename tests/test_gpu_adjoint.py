@@ -55,6 +55,27 @@ def test_adjoint_same_state(cell, u_dtype, B, L, D):
 
 
 @pytest.mark.parametrize("cell", ["gru", "lstm"])
+def test_adjoint_whole_chunks(cell):
+    """L a whole number of the launch's chunks and D of its channel tiles:
+    every workgroup, the last chunk's included, runs the unmasked full-tile
+    path, whose lanes read the state row before their first step from the
+    neighbouring lane's rows and the previous chunk."""
+    B = 2
+    pl = binding.plan(cell, binding.OP_ADJOINT, B, 1000, 256)
+    L, D = 3 * pl["chunk"], 2 * pl["channels"]
+    say(f"adjoint {cell} B={B} L={L} D={D} (whole chunks of {pl['chunk']} steps, {pl['channels']} channels)")
+    x = make_inputs(cell, B, L, D, seed=2500 + L, u_dtype="bf16", adjoint=True)
+    S, _ = O.newton(cell, x.u, x.a, K=3)
+    S32 = S.astype(np.float32).astype(np.float64)
+    du, ds0, da = O.adjoint(cell, x.u, x.a, S32, x.dh)
+    g = _gpu_adjoint(cell, x, S32)
+    assert_close(g["du"], du, GRAD_TOL, "du")
+    assert_close(g["ds0"], ds0, GRAD_TOL, "ds0")
+    scale = max(1.0, float(np.abs(da).max()))
+    assert_close(g["da"], da, GRAD_TOL * scale, "da")
+
+
+@pytest.mark.parametrize("cell", ["gru", "lstm"])
 def test_adjoint_end_to_end(cell):
     say(f"adjoint {cell} end to end")
     B, L, D = 2, 2000, 128
