@@ -42,6 +42,14 @@ struct FusedCfg;
 template <> struct FusedCfg<GruCell, 2> { static constexpr int T = 16, W = 4, LL = 4, OCC = 3; static constexpr int UMODE = 2; };
 template <> struct FusedCfg<GruCell, 1> { static constexpr int T = 16, W = 4, LL = 1, OCC = 2; static constexpr int UMODE = 1; };
 template <> struct FusedCfg<LstmCell, 1> { static constexpr int T = 11, W = 4, LL = 2, OCC = 3; static constexpr int UMODE = 3; };
+// Problems that would give the shape above only a few workgroups (under half
+// as many as the GPU has CUs) are latency-bound: short lanes over narrow
+// channel tiles let more workgroups share the steps (the two-channel GRU
+// only; it measured faster up to 96 regular workgroups, slower from 192).
+template <class Cell, int C>
+struct FusedSmallCfg;
+template <> struct FusedSmallCfg<GruCell, 2> { static constexpr int T = 4, W = 4, LL = 8, OCC = 3; static constexpr int UMODE = 2; };
+constexpr long long kSmallGrid = 128;  // workgroups of the regular shape below which the small one is used
 
 // Iteration 1 (no state input, lighter cell form): same chunk length and
 // channel tile, its own split into waves and steps.
@@ -109,21 +117,31 @@ Geo geo_for_c(int C) {
   return geo<Cell, 1, ADJ>();
 }
 
-template <class Cell, int C>
-constexpr Geo fused_geo() {
-  using K = FusedCfg<Cell, C>;
+template <class K, int C>
+constexpr Geo fused_geo_of() {
   return Geo{K::T * K::W * K::LL, (64 / K::LL) * C, K::W};
 }
 
 template <class Cell>
 Geo fused_geo_for_c(int C) {
   if constexpr (max_c<Cell, false>() >= 2) {
-    if (C == 2) return fused_geo<Cell, 2>();
+    if (C == 2) return fused_geo_of<FusedCfg<Cell, 2>, 2>();
   }
-  return fused_geo<Cell, 1>();
+  return fused_geo_of<FusedCfg<Cell, 1>, 1>();
 }
 
-Geo fused_geo_for(int cell, int C) {
+long long ceil_div(long long a, long long b);
+
+// whether a fused solve runs the small-problem shape: the two-channel GRU
+// when the regular shape would launch fewer than kSmallGrid workgroups
+bool fused_small(int cell, int C, const pararnn_opts* o) {
+  if (cell != PARARNN_GRU || C != 2) return false;
+  const Geo g = fused_geo_for_c<GruCell>(2);
+  return static_cast<long long>(o->B) * ceil_div(o->D, g.cw) * ceil_div(o->L, g.chunk) < kSmallGrid;
+}
+
+Geo fused_geo_for(int cell, int C, const pararnn_opts* o) {
+  if (fused_small(cell, C, o)) return fused_geo_of<FusedSmallCfg<GruCell, 2>, 2>();
   return cell == PARARNN_LSTM ? fused_geo_for_c<LstmCell>(C) : fused_geo_for_c<GruCell>(C);
 }
 
@@ -174,7 +192,7 @@ bool opts_ok(int cell, int op, const pararnn_opts* o) {
   for (int C = 1; C <= cmax_for(cell, op); C *= 2) {
     // both schedules of the solve: the per-iteration and the fused geometry
     for (int fused = 0; fused <= (op == PARARNN_OP_SOLVE ? 1 : 0); ++fused) {
-      const Geo g = fused ? fused_geo_for(cell, C) : geo_for(cell, op, C);
+      const Geo g = fused ? fused_geo_for(cell, C, o) : geo_for(cell, op, C);
       const double wgs = static_cast<double>(o->B) * ceil_div(o->D, g.cw) * ceil_div(o->L, g.chunk);
       if (wgs > 2.0e9) return false;
     }
@@ -433,9 +451,8 @@ bool use_fused(const pararnn_opts* o) {
   return o->schedule == PARARNN_SCHEDULE_FUSED || (o->schedule == PARARNN_SCHEDULE_AUTO && !o->early_exit);
 }
 
-template <class Cell, class UT, int C, bool INCL>
+template <class K, class Cell, class UT, int C, bool INCL>
 int launch_fused(const FusedArgs& a, hipStream_t s, Stamps t) {
-  using K = FusedCfg<Cell, C>;
   // fp32 gate inputs would take twice the workgroup memory: stream them instead
   constexpr int UM = (K::UMODE == 2 && sizeof(UT) > 2) ? 0 : K::UMODE;
   const unsigned grid = static_cast<unsigned>(a.B) * a.ntiles_d * static_cast<unsigned>(a.nchunks);
@@ -444,23 +461,28 @@ int launch_fused(const FusedArgs& a, hipStream_t s, Stamps t) {
                 dim3(64 * K::W), s, t, b);
 }
 
-template <class Cell, class UT, int C>
+template <class K, class Cell, class UT, int C>
 int launch_fused_mode(bool incl, const FusedArgs& a, hipStream_t s, Stamps t) {
-  return incl ? launch_fused<Cell, UT, C, true>(a, s, t) : launch_fused<Cell, UT, C, false>(a, s, t);
+  return incl ? launch_fused<K, Cell, UT, C, true>(a, s, t) : launch_fused<K, Cell, UT, C, false>(a, s, t);
 }
 
 template <class Cell, class UT>
-int launch_fused_c(int C, bool incl, const FusedArgs& a, hipStream_t s, Stamps t) {
+int launch_fused_c(int C, bool small, bool incl, const FusedArgs& a, hipStream_t s, Stamps t) {
   if constexpr (max_c<Cell, false>() >= 2) {
-    if (C == 2) return launch_fused_mode<Cell, UT, 2>(incl, a, s, t);
+    if (C == 2) {
+      if constexpr (Cell::NS == 1) {
+        if (small) return launch_fused_mode<FusedSmallCfg<Cell, 2>, Cell, UT, 2>(incl, a, s, t);
+      }
+      return launch_fused_mode<FusedCfg<Cell, 2>, Cell, UT, 2>(incl, a, s, t);
+    }
   }
-  return launch_fused_mode<Cell, UT, 1>(incl, a, s, t);
+  return launch_fused_mode<FusedCfg<Cell, 1>, Cell, UT, 1>(incl, a, s, t);
 }
 
 template <class Cell>
-int launch_fused_any(int dtype, int C, bool incl, const FusedArgs& a, hipStream_t s, Stamps t) {
-  return dtype == PARARNN_BF16 ? launch_fused_c<Cell, bf16>(C, incl, a, s, t)
-                               : launch_fused_c<Cell, float>(C, incl, a, s, t);
+int launch_fused_any(int dtype, int C, bool small, bool incl, const FusedArgs& a, hipStream_t s, Stamps t) {
+  return dtype == PARARNN_BF16 ? launch_fused_c<Cell, bf16>(C, small, incl, a, s, t)
+                               : launch_fused_c<Cell, float>(C, small, incl, a, s, t);
 }
 
 
@@ -475,7 +497,7 @@ int solve(int cell, const void* u, const float* a, const float* c0, const float*
   const int C = pick_c(cmax_for(cell, PARARNN_OP_SOLVE), o->D, usize, u, {a, h0, h, c0, c});
   if (!C || !aligned(u, usize)) return PARARNN_EUNSUPPORTED;
   const bool fused = use_fused(o);
-  const Geo g = fused ? fused_geo_for(cell, C) : geo_for(cell, PARARNN_OP_SOLVE, C);
+  const Geo g = fused ? fused_geo_for(cell, C, o) : geo_for(cell, PARARNN_OP_SOLVE, C);
   // one chunk of gate inputs (and of states) is addressed with 32-bit offsets below 2^31
   if (static_cast<double>(g.chunk) * ngates(cell) * o->D * 4.0 >= 2147483648.0) return PARARNN_EUNSUPPORTED;
   const Layout y = layout(cell, PARARNN_OP_SOLVE, o, false, g, fused);
@@ -512,8 +534,9 @@ int solve(int cell, const void* u, const float* a, const float* c0, const float*
     fa.ntiles_d = y.ntiles_d;
     // the one launch stamps events 1 and 2; iterations 2..K end with it
     const Stamps t = stamps(o, 1, 2);
-    rc = (cell == PARARNN_LSTM) ? launch_fused_any<LstmCell>(o->u_dtype, C, incl_only, fa, stream, t)
-                                : launch_fused_any<GruCell>(o->u_dtype, C, incl_only, fa, stream, t);
+    const bool small = fused_small(cell, C, o);
+    rc = (cell == PARARNN_LSTM) ? launch_fused_any<LstmCell>(o->u_dtype, C, small, incl_only, fa, stream, t)
+                                : launch_fused_any<GruCell>(o->u_dtype, C, small, incl_only, fa, stream, t);
     if (rc) return rc;
     for (int k = 2; k <= K; ++k) {
       rc = record(o, k + 1, stream);
@@ -691,7 +714,7 @@ extern "C" size_t pararnn_workspace_bytes(int32_t cell, int32_t op, const pararn
   const bool fused = op == PARARNN_OP_SOLVE && use_fused(o);
   size_t n = 0;
   for (int C = 1; C <= cmax_for(cell, op); C *= 2) {
-    const Geo g = fused ? fused_geo_for(cell, C) : geo_for(cell, op, C);
+    const Geo g = fused ? fused_geo_for(cell, C, o) : geo_for(cell, op, C);
     const size_t t = layout(cell, op, o, true, g, fused).total;
     n = t > n ? t : n;
   }
@@ -740,7 +763,7 @@ extern "C" int32_t pararnn_plan_query(int32_t cell, int32_t op, const pararnn_op
   // every pointer 16-byte aligned: the widest channel group that divides D
   alignas(16) static const char kAligned[16] = {0};
   const int C = pick_c(cmax_for(gcell, op), o->D, usize, kAligned, {});
-  const Geo g = fused ? fused_geo_for(cell, C) : geo_for(gcell, op, C);
+  const Geo g = fused ? fused_geo_for(cell, C, o) : geo_for(gcell, op, C);
   const Layout y = layout(gcell, op, o, false, g, fused);
   plan->vec = C;
   plan->chunk = g.chunk;

@@ -192,7 +192,15 @@ def test_plan_query_carry_modes(lib):
     pl = b.plan
     # fused solve: 32-channel tiles, inclusive only from 64 tiles per row
     assert pl("gru", b.OP_SOLVE, 1, 700, 2048)["inclusive_only"] == 1
-    assert pl("gru", b.OP_SOLVE, 1, 700, 1024)["inclusive_only"] == 0
+    assert pl("gru", b.OP_SOLVE, 1, 2048, 1024)["inclusive_only"] == 0
+    # the GRU's small-problem shape below 128 workgroups of the regular one:
+    # 16-channel tiles of 128 steps, the same threshold of 64 tiles per row
+    for B, L, D, incl in ((1, 700, 1024, 1), (1, 700, 512, 0), (1, 1024, 64, 0)):
+        p = pl("gru", b.OP_SOLVE, B, L, D)
+        assert (p["channels"], p["chunk"], p["inclusive_only"]) == (16, 128, incl), (B, L, D, p)
+    for B, L, D in ((2, 700, 1024), (1, 700, 2048), (8, 4096, 1024)):
+        assert pl("gru", b.OP_SOLVE, B, L, D)["channels"] == 32, (B, L, D)
+    assert pl("gru", b.OP_SOLVE, 1, 700, 1023)["channels"] == 64  # odd D: one channel per lane, no small shape
     p = pl("lstm", b.OP_SOLVE, 1, 700, 2048)
     assert p["inclusive_only"] == 1 and p["fused"] == 1 and p["channels"] == 32
     # per-iteration schedule: 64-channel tiles; GRU from 128, LSTM from 64 tiles per row

@@ -29,7 +29,9 @@ DEV = torch.device("cuda:0")
 
 # (cell, schedule, B, L, D, inclusive_only expected)
 SOLVE_MODES = [
-    ("gru", "fused", 1, 700, 2048, 1), ("gru", "fused", 1, 700, 1024, 0),
+    ("gru", "fused", 1, 700, 2048, 1), ("gru", "fused", 1, 2048, 1024, 0),
+    # the GRU's small-problem shape (16-channel tiles), both carry modes
+    ("gru", "fused", 1, 700, 1024, 1), ("gru", "fused", 1, 700, 512, 0),
     ("lstm", "fused", 1, 700, 2048, 1), ("lstm", "fused", 1, 700, 1024, 0),
     ("gru", "per_iteration", 2, 700, 4096, 1), ("gru", "per_iteration", 1, 700, 4096, 0),
     ("lstm", "per_iteration", 1, 700, 4096, 1), ("lstm", "per_iteration", 1, 700, 2048, 0),
@@ -171,19 +173,22 @@ def test_gru_jacobian_near_one_over_long_sequence():
 
 
 def test_gru_iterate_overflow_is_flagged_not_an_error():
-    """a_c = 8, u_z = 0, u_r = 5, u_c = 0: at the zero iterate every Jacobian
-    is about 0.5 + 0.5 * 8 = 4.5, so the first Newton update grows like 4.5^l
-    and passes the fp32 range near l = 59 (the fp64 oracle, with its wider
-    range, stays finite over L = 200). The solve still returns OK; a row
-    whose states are not all finite reports a non-finite row maximum and is not
-    converged; a finite row matches the oracle to 1e-4 relative."""
+    """a_c = 8, u_z = 0, u_r = 5, u_c = 0.1: at the zero iterate the residual
+    is z c~ = 0.5 tanh(0.1), about 0.05, and every Jacobian is about
+    0.5 + 0.5 * 8 * 0.99 = 4.4, so the first Newton update grows like 4.4^l and
+    passes the fp32 range near l = 62 (the fp64 oracle, with its wider range,
+    stays finite over L = 200). The solve still returns OK; a row whose states
+    are not all finite reports a non-finite row maximum and is not converged; a
+    finite row matches the oracle to 1e-4 relative."""
     B, L, D = 2, 200, 64
     say(f"stress gru overflow B={B} L={L} D={D}")
     u = torch.zeros(B, L, 3, D)
     u[:, :, 1, :] = 5.0
+    u[:, :, 2, :] = 0.1
     a = torch.zeros(3, D)
     a[2] = 8.0
     want, upd = O.newton("gru", u, a, K=3)
+    assert np.isfinite(want).all() and np.abs(want).max() > 1e38  # beyond fp32, not fp64
     r = binding.solve("gru", u.to(DEV), a.to(DEV), iters=3)  # raises on a non-zero status
     torch.cuda.synchronize()
     got = r["h"].cpu().double().numpy()
@@ -198,3 +203,30 @@ def test_gru_iterate_overflow_is_flagged_not_an_error():
             assert not np.isfinite(mu[:, b]).all(), f"row {b}: non-finite states but finite row maxima"
             assert conv[b] == 0
     assert not np.isfinite(got).all(), "expected the fp32 iterate to overflow on this input"
+
+
+@pytest.mark.parametrize("B,L,D", [(2, 200, 64), (2, 4096, 1024)])
+def test_gru_zero_update_with_growing_jacobians(B, L, D):
+    """u_c = 0 instead: the zero state is a fixed point of the cell, so the
+    residual at the zero iterate is exactly 0 and so is every Newton update,
+    while the Jacobians stay near 4.5. The scan composes products of Jacobians
+    over a wave's steps (32 in the GRU's small-problem shape, 64 in the
+    regular one); 4.5^64 passes the fp32 range, and such an infinite product
+    applied to the zero carry gives inf * 0 = NaN. Either way no row may come
+    back finite and wrong: a row is exactly 0 and converged, or it is
+    non-finite, with a non-finite row maximum, and not converged."""
+    say(f"stress gru zero update B={B} L={L} D={D} (plan {binding.plan('gru', binding.OP_SOLVE, B, L, D)})")
+    u = torch.zeros(B, L, 3, D)
+    u[:, :, 1, :] = 5.0
+    a = torch.zeros(3, D)
+    a[2] = 8.0
+    r = binding.solve("gru", u.to(DEV), a.to(DEV), iters=3)
+    torch.cuda.synchronize()
+    got = r["h"].cpu().double().numpy()
+    mu = r["max_update"].cpu().double().numpy()
+    conv = r["converged"].cpu().numpy()
+    for b in range(B):
+        if np.isfinite(got[b]).all():
+            assert np.all(got[b] == 0.0) and np.all(mu[:, b] == 0.0) and conv[b] == 1, f"row {b}"
+        else:
+            assert not np.isfinite(mu[:, b]).all() and conv[b] == 0, f"row {b}"
