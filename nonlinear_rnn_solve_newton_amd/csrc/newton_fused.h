@@ -202,6 +202,22 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_fused_kernel(const FusedAr
     typename Cell::Jac Jt[T][C];
     float rt[T][NS][C];
     Aff<NS, C> acc;  // the lane's transform over its steps, from its first step
+    // gate inputs held in workgroup memory (UMODE 2, 3) are read one step
+    // ahead of their use, so that each read has a whole step of cell work to
+    // complete behind
+    URaw<UT, C> un[UMODE == 2 ? G : 1];
+    float uns[UMODE == 3 ? G : 1][C];
+    auto fetch = [&](int tt) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        if constexpr (UMODE == 2) un[g].get_lds(su + (tt * G + g) * USEG);
+        else if constexpr (UMODE == 3) {
+#pragma unroll
+          for (int c = 0; c < C; ++c) uns[g][c] = sus[(tt * G + g) * USEG + c];
+        }
+      }
+    };
+    if constexpr (UMODE >= 2) fetch(0);
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       if (t == TPOLL) {
@@ -221,13 +237,16 @@ __global__ void __launch_bounds__(64 * W, OCC) newton_fused_kernel(const FusedAr
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         if constexpr (UMODE == 1) ut[g] = uu[t][g];
-        else if constexpr (UMODE == 2) ut[g].get_lds(su + (t * G + g) * USEG);
+        else if constexpr (UMODE == 2) ut[g] = un[g];
         else if constexpr (UMODE == 3) {
 #pragma unroll
-          for (int c = 0; c < C; ++c) uts[g][c] = sus[(t * G + g) * USEG + c];
+          for (int c = 0; c < C; ++c) uts[g][c] = uns[g][c];
         } else {
           ut[g].load(ru, vu0 + t * ustep, static_cast<uint32_t>(g) * gstep);
         }
+      }
+      if constexpr (UMODE >= 2) {
+        if (t + 1 < T) fetch(t + 1);
       }
 #pragma unroll
       for (int c = 0; c < C; ++c) {
