@@ -42,13 +42,15 @@ struct FusedCfg;
 template <> struct FusedCfg<GruCell, 2> { static constexpr int T = 16, W = 4, LL = 4, OCC = 3; static constexpr int UMODE = 2; };
 template <> struct FusedCfg<GruCell, 1> { static constexpr int T = 16, W = 4, LL = 1, OCC = 2; static constexpr int UMODE = 1; };
 template <> struct FusedCfg<LstmCell, 1> { static constexpr int T = 11, W = 4, LL = 2, OCC = 3; static constexpr int UMODE = 3; };
-// Problems that would give the shape above only a few workgroups (under half
-// as many as the GPU has CUs) are latency-bound: short lanes over narrow
-// channel tiles let more workgroups share the steps (the two-channel GRU
-// only; it measured faster up to 96 regular workgroups, slower from 192).
+// Problems that would give the shapes above only a few workgroups (under
+// half as many as the GPU has CUs) are latency-bound: short lanes over narrow
+// channel tiles let more workgroups share the steps (the two-channel GRU and
+// the LSTM; both measured faster up to 96 regular workgroups, and slower from
+// 168 to 192 on).
 template <class Cell, int C>
 struct FusedSmallCfg;
 template <> struct FusedSmallCfg<GruCell, 2> { static constexpr int T = 4, W = 4, LL = 8, OCC = 3; static constexpr int UMODE = 2; };
+template <> struct FusedSmallCfg<LstmCell, 1> { static constexpr int T = 4, W = 4, LL = 8, OCC = 3; static constexpr int UMODE = 3; };
 constexpr long long kSmallGrid = 128;  // workgroups of the regular shape below which the small one is used
 
 // Iteration 1 (no state input, lighter cell form): same chunk length and
@@ -132,16 +134,19 @@ Geo fused_geo_for_c(int C) {
 
 long long ceil_div(long long a, long long b);
 
-// whether a fused solve runs the small-problem shape: the two-channel GRU
-// when the regular shape would launch fewer than kSmallGrid workgroups
+// whether a fused solve runs the small-problem shape: the two-channel GRU and
+// the LSTM, when the regular shape would launch only a few workgroups
 bool fused_small(int cell, int C, const pararnn_opts* o) {
-  if (cell != PARARNN_GRU || C != 2) return false;
-  const Geo g = fused_geo_for_c<GruCell>(2);
+  const bool lstm = cell == PARARNN_LSTM;
+  if (lstm ? C != 1 : C != 2) return false;
+  const Geo g = lstm ? fused_geo_for_c<LstmCell>(1) : fused_geo_for_c<GruCell>(2);
   return static_cast<long long>(o->B) * ceil_div(o->D, g.cw) * ceil_div(o->L, g.chunk) < kSmallGrid;
 }
 
 Geo fused_geo_for(int cell, int C, const pararnn_opts* o) {
-  if (fused_small(cell, C, o)) return fused_geo_of<FusedSmallCfg<GruCell, 2>, 2>();
+  if (fused_small(cell, C, o))
+    return cell == PARARNN_LSTM ? fused_geo_of<FusedSmallCfg<LstmCell, 1>, 1>()
+                                : fused_geo_of<FusedSmallCfg<GruCell, 2>, 2>();
   return cell == PARARNN_LSTM ? fused_geo_for_c<LstmCell>(C) : fused_geo_for_c<GruCell>(C);
 }
 
@@ -453,8 +458,11 @@ bool use_fused(const pararnn_opts* o) {
 
 template <class K, class Cell, class UT, int C, bool INCL>
 int launch_fused(const FusedArgs& a, hipStream_t s, Stamps t) {
-  // fp32 gate inputs would take twice the workgroup memory: stream them instead
-  constexpr int UM = (K::UMODE == 2 && sizeof(UT) > 2) ? 0 : K::UMODE;
+  // gate inputs in workgroup memory (UMODE 2) unless they would take more than
+  // 64 KB of it there (fp32 inputs in the regular shapes): stream them instead
+  constexpr int USEG = (64 / K::LL) * C;
+  constexpr size_t ULDS = static_cast<size_t>(K::W) * K::LL * (K::T * Cell::G * USEG + USEG) * sizeof(UT);
+  constexpr int UM = (K::UMODE == 2 && ULDS > 65536) ? 0 : K::UMODE;
   const unsigned grid = static_cast<unsigned>(a.B) * a.ntiles_d * static_cast<unsigned>(a.nchunks);
   const FusedArgs& b = a;
   return launch(newton_fused_kernel<Cell, UT, C, K::T, K::W, K::LL, K::OCC, UM, INCL>, dim3(grid),
@@ -475,6 +483,9 @@ int launch_fused_c(int C, bool small, bool incl, const FusedArgs& a, hipStream_t
       }
       return launch_fused_mode<FusedCfg<Cell, 2>, Cell, UT, 2>(incl, a, s, t);
     }
+  }
+  if constexpr (Cell::NS == 2) {
+    if (small) return launch_fused_mode<FusedSmallCfg<Cell, 1>, Cell, UT, 1>(incl, a, s, t);
   }
   return launch_fused_mode<FusedCfg<Cell, 1>, Cell, UT, 1>(incl, a, s, t);
 }

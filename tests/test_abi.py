@@ -201,6 +201,12 @@ def test_plan_query_carry_modes(lib):
     for B, L, D in ((2, 700, 1024), (1, 700, 2048), (8, 4096, 1024)):
         assert pl("gru", b.OP_SOLVE, B, L, D)["channels"] == 32, (B, L, D)
     assert pl("gru", b.OP_SOLVE, 1, 700, 1023)["channels"] == 64  # odd D: one channel per lane, no small shape
+    # the LSTM's small-problem shape: 8-channel tiles of 128 steps
+    for B, L, D, incl in ((1, 600, 512, 1), (1, 1000, 256, 0), (1, 1024, 64, 0)):
+        p = pl("lstm", b.OP_SOLVE, B, L, D)
+        assert (p["channels"], p["chunk"], p["inclusive_only"]) == (8, 128, incl), (B, L, D, p)
+    for B, L, D in ((2, 1000, 200), (1, 700, 512), (1, 700, 1024)):
+        assert pl("lstm", b.OP_SOLVE, B, L, D)["channels"] == 32, (B, L, D)
     p = pl("lstm", b.OP_SOLVE, 1, 700, 2048)
     assert p["inclusive_only"] == 1 and p["fused"] == 1 and p["channels"] == 32
     # per-iteration schedule: 64-channel tiles; GRU from 128, LSTM from 64 tiles per row

@@ -33,6 +33,8 @@ SOLVE_MODES = [
     # the GRU's small-problem shape (16-channel tiles), both carry modes
     ("gru", "fused", 1, 700, 1024, 1), ("gru", "fused", 1, 700, 512, 0),
     ("lstm", "fused", 1, 700, 2048, 1), ("lstm", "fused", 1, 700, 1024, 0),
+    # the LSTM's small-problem shape (8-channel tiles), both carry modes
+    ("lstm", "fused", 1, 600, 512, 1), ("lstm", "fused", 1, 1000, 256, 0),
     ("gru", "per_iteration", 2, 700, 4096, 1), ("gru", "per_iteration", 1, 700, 4096, 0),
     ("lstm", "per_iteration", 1, 700, 4096, 1), ("lstm", "per_iteration", 1, 700, 2048, 0),
 ]
