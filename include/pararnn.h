@@ -132,11 +132,13 @@ int32_t pararnn_solve_gru(const void* u, const float* a, const float* h0, float*
  * array's device address (hipGetSymbolAddress) with that GPU current.
  * Arguments, outputs, asynchrony and numerics are those of pararnn_solve_gru.
  * Errors: as for pararnn_solve_gru; PARARNN_ESCRATCH, before any HIP call,
- * when pararnn_workspace_bytes(PARARNN_GRU, PARARNN_OP_SOLVE, o) exceeds the
- * scratch size. Every call on one GPU uses that GPU's one array, and each
- * call resets what must start at zero; calls on one GPU must therefore be
- * ordered (one stream, or synchronised): calls that overlap in time race on
- * the array and give wrong results. */
+ * when the workspace of the launch the call makes exceeds the scratch size
+ * (that launch's channel group follows from D and the pointers' alignment;
+ * pararnn_workspace_bytes(PARARNN_GRU, PARARNN_OP_SOLVE, o), which covers
+ * every channel group, bounds it from above). Every call on one GPU uses
+ * that GPU's one array, and each call resets what must start at zero; calls
+ * on one GPU must therefore be ordered (one stream, or synchronised): calls
+ * that overlap in time race on the array and give wrong results. */
 int32_t pararnn_solve_gru_scratch(const void* u, const float* a, const float* h0, float* h,
                                   const pararnn_opts* o, int32_t* iters, int32_t* converged,
                                   float* max_update, void* stream);

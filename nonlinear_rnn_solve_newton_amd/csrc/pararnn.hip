@@ -497,21 +497,43 @@ int launch_fused_any(int dtype, int C, bool small, bool incl, const FusedArgs& a
 }
 
 
-int solve(int cell, const void* u, const float* a, const float* c0, const float* h0, float* c, float* h,
-          void* ws, size_t ws_bytes, const pararnn_opts* o, int32_t* iters, int32_t* converged,
-          float* max_update, hipStream_t stream) {
+// The launch plan of a solve call: the channel group its pointers allow, the
+// schedule, the launch shape and the workspace layout. Returns the status the
+// call gives before any launch (every check that needs no workspace).
+struct SolvePlan {
+  int C = 0;
+  bool fused = false;
+  Geo g{};
+  Layout y{};
+};
+int solve_plan(int cell, const void* u, const float* a, const float* c0, const float* h0, const float* c,
+               const float* h, const pararnn_opts* o, SolvePlan* sp) {
   if (!opts_ok(cell, PARARNN_OP_SOLVE, o)) return PARARNN_EINVAL;
-  if (!u || !a || !h || !ws || (cell == PARARNN_LSTM && !c)) return PARARNN_EINVAL;
+  if (!u || !a || !h || (cell == PARARNN_LSTM && !c)) return PARARNN_EINVAL;
   if (o->u_dtype != PARARNN_F32 && o->u_dtype != PARARNN_BF16) return PARARNN_EUNSUPPORTED;
   if (o->early_exit != 0 && o->early_exit != 1) return PARARNN_EINVAL;
   const size_t usize = o->u_dtype == PARARNN_BF16 ? 2 : 4;
-  const int C = pick_c(cmax_for(cell, PARARNN_OP_SOLVE), o->D, usize, u, {a, h0, h, c0, c});
-  if (!C || !aligned(u, usize)) return PARARNN_EUNSUPPORTED;
-  const bool fused = use_fused(o);
-  const Geo g = fused ? fused_geo_for(cell, C, o) : geo_for(cell, PARARNN_OP_SOLVE, C);
+  sp->C = pick_c(cmax_for(cell, PARARNN_OP_SOLVE), o->D, usize, u, {a, h0, h, c0, c});
+  if (!sp->C || !aligned(u, usize)) return PARARNN_EUNSUPPORTED;
+  sp->fused = use_fused(o);
+  sp->g = sp->fused ? fused_geo_for(cell, sp->C, o) : geo_for(cell, PARARNN_OP_SOLVE, sp->C);
   // one chunk of gate inputs (and of states) is addressed with 32-bit offsets below 2^31
-  if (static_cast<double>(g.chunk) * ngates(cell) * o->D * 4.0 >= 2147483648.0) return PARARNN_EUNSUPPORTED;
-  const Layout y = layout(cell, PARARNN_OP_SOLVE, o, false, g, fused);
+  if (static_cast<double>(sp->g.chunk) * ngates(cell) * o->D * 4.0 >= 2147483648.0) return PARARNN_EUNSUPPORTED;
+  sp->y = layout(cell, PARARNN_OP_SOLVE, o, false, sp->g, sp->fused);
+  return PARARNN_OK;
+}
+
+int solve(int cell, const void* u, const float* a, const float* c0, const float* h0, float* c, float* h,
+          void* ws, size_t ws_bytes, const pararnn_opts* o, int32_t* iters, int32_t* converged,
+          float* max_update, hipStream_t stream) {
+  SolvePlan sp;
+  const int prc = solve_plan(cell, u, a, c0, h0, c, h, o, &sp);
+  if (prc) return prc;
+  if (!ws) return PARARNN_EINVAL;
+  const int C = sp.C;
+  const bool fused = sp.fused;
+  const Geo g = sp.g;
+  const Layout y = sp.y;
   if (ws_bytes < y.total) return PARARNN_EWORKSPACE;
   if (!aligned(ws, kAlign)) return PARARNN_EUNSUPPORTED;
 
@@ -792,10 +814,12 @@ extern "C" int32_t pararnn_solve_gru_scratch(const void* u, const float* a, cons
                                              const pararnn_opts* o, int32_t* iters, int32_t* converged,
                                              float* max_update, void* stream_) {
   // every check that needs no device comes first, so that a rejected call
-  // makes no HIP call at all
-  const size_t need = pararnn_workspace_bytes(PARARNN_GRU, PARARNN_OP_SOLVE, o);
-  if (need == 0 || !u || !a || !h) return PARARNN_EINVAL;
-  if (need > kScratchBytes) return PARARNN_ESCRATCH;
+  // makes no HIP call at all; the workspace needed is that of the launch
+  // this call makes (its pointers fix the channel group)
+  SolvePlan sp;
+  const int prc = solve_plan(PARARNN_GRU, u, a, nullptr, h0, nullptr, h, o, &sp);
+  if (prc) return prc;
+  if (sp.y.total > kScratchBytes) return PARARNN_ESCRATCH;
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   void* ws = nullptr;
   const int rc = scratch_ptr(stream, &ws);

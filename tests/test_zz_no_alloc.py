@@ -53,6 +53,24 @@ def test_scratch_solve_matches_workspace_solve(schedule):
         say(f"  vs workspace {err:.2e}, vs oracle {oerr:.2e}")
 
 
+def test_scratch_solve_sizes_for_its_own_launch():
+    """The long GRU workload (B=1 L=65536 D=2048) fits: its two-channel fused
+    launch needs 38 MB of the 64 MiB scratch, though pararnn_workspace_bytes,
+    which also covers the one-channel launch, asks for 152 MB. The result
+    equals the workspace call's bit for bit (inclusive-only carries)."""
+    dev = torch.device("cuda:0")
+    B, L, D = 1, 65536, 2048
+    assert binding.plan("gru", binding.OP_SOLVE, B, L, D)["inclusive_only"] == 1
+    say(f"scratch solve: gru B={B} L={L} D={D} fused")
+    x = make_inputs("gru", B, L, D, seed=77, u_dtype="bf16")
+    u, a = x.u.to(dev), x.a.to(dev)
+    ref = binding.solve("gru", u, a, iters=3, schedule="fused")
+    got = binding.solve_gru_scratch(u, a, iters=3, schedule="fused")
+    torch.cuda.synchronize()
+    assert torch.equal(got["h"], ref["h"]) and torch.equal(got["converged"], ref["converged"])
+    assert torch.equal(got["max_update"], ref["max_update"])
+
+
 def test_scratch_solve_rejects_oversized_problem():
     """A problem whose workspace exceeds the scratch is refused before any launch."""
     dev = torch.device("cuda:0")
