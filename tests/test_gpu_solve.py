@@ -22,6 +22,33 @@ SHAPES = [
 ]
 
 
+# (cell, B, L, D): one schedule solves the sequence as a single chunk, the
+# other over two chunks (LSTM: fused chunks of 88 steps against one 96-step
+# per-iteration chunk; GRU: one 256-step fused chunk against per-iteration
+# chunks of 128)
+CHUNKINGS = [("lstm", 2, 96, 1024), ("gru", 4, 256, 1024)]
+
+
+@pytest.mark.parametrize("cell,B,L,D", CHUNKINGS, ids=[f"{c}-{b}x{l}x{d}" for c, b, l, d in CHUNKINGS])
+def test_chunked_equals_single_chunk(cell, B, L, D):
+    """The chunked path equals the single-chunk path on the same input within
+    1e-6: the carry across the chunk boundary adds only rounding."""
+    counts = {s: binding.plan(cell, binding.OP_SOLVE, B, L, D, schedule=s)["nchunks"]
+              for s in ("fused", "per_iteration")}
+    assert sorted(counts.values())[0] == 1 and sorted(counts.values())[1] >= 2, counts
+    say(f"{cell} B={B} L={L} D={D}: chunks per schedule {counts}")
+    x = make_inputs(cell, B, L, D, seed=900 + L, u_dtype="bf16")
+    dev = torch.device("cuda:0")
+    u, a = x.u.to(dev), x.a.to(dev)
+    r = {s: binding.solve(cell, u, a, iters=3, schedule=s) for s in counts}
+    torch.cuda.synchronize()
+    for comp in (["h"] if cell == "gru" else ["c", "h"]):
+        f = r["fused"][comp].cpu().double().numpy()
+        q = r["per_iteration"][comp].cpu().double().numpy()
+        scale = np.maximum(1.0, np.abs(f))
+        assert np.all(np.abs(f - q) <= 1e-6 * scale), f"{comp}: max {np.abs(f - q).max():.2e}"
+
+
 @pytest.mark.parametrize("schedule", ["fused", "per_iteration"])
 @pytest.mark.parametrize("cell", ["gru", "lstm"])
 @pytest.mark.parametrize("u_dtype", ["f32", "bf16"])
