@@ -174,6 +174,39 @@ def test_gru_jacobian_near_one_over_long_sequence():
     check_flags(int(r["iters"].item()), r["converged"].cpu().numpy(), upd, 3, 1e-4)
 
 
+def test_block2_scan_near_unit_products_over_long_sequence():
+    """The 2x2 scan with the LSTM's Jacobian pattern at the edge of stability:
+    A = [[1 - 2^-16, 0], [q, 0]] (eigenvalues 1 - 2^-16 and 0, exactly
+    representable), q ~ U(0, 0.5), b ~ N(0, 1), over 65536 steps. The first
+    component sums its inputs over all of them (a random walk up to a few
+    hundred), so the chunk and lane aggregates are products of thousands of
+    near-unit blocks. They stay finite, and every element matches the fp64
+    scan to 1e-4 of its series' largest magnitude. That is the bar here, not
+    1e-4 of each value: the scan's fp32 products of near-unit factors drop a
+    term below half an ulp at every factor (a bias of about 2^-25 each) and
+    the carry, some hundreds here, is multiplied by them at each of the 1024
+    chunk hand-offs (measured: 4.6e-5 of the series' largest magnitude, where
+    a sequential fp32 recurrence, which forms no products, is off by about
+    1.6e-6 of it). An LSTM solve with a forget gate that close to 1 is limited
+    by fp32 even before the scan: the gate's own rounding, about 6e-8, is 0.6%
+    of its distance from 1."""
+    B, L, D = 1, 65536, 64
+    say(f"stress block2 scan, a = 1 - 2^-16, B={B} L={L} D={D} (plan {binding.plan('gru', binding.OP_SCAN_BLOCK2, B, L, D)})")
+    g = torch.Generator().manual_seed(3700)
+    A = torch.zeros(2, 2, B, L, D)
+    A[0, 0] = 1.0 - 2.0 ** -16
+    A[1, 0] = 0.5 * torch.rand(B, L, D, generator=g)
+    bb = torch.randn(2, B, L, D, generator=g)
+    r = binding.scan(A.to(DEV), bb.to(DEV))
+    torch.cuda.synchronize()
+    got = r["s"].cpu().double().numpy()
+    want = O.scan(A, bb)
+    assert np.isfinite(got).all() and np.abs(want).max() > 50
+    scale = np.maximum(1.0, np.abs(want).max(axis=2, keepdims=True))  # per (component, row, channel) series
+    rel = np.abs(got - want) / scale
+    assert np.all(rel <= 1e-4), f"max error {rel.max():.2e} of the series' largest magnitude"
+
+
 def test_gru_iterate_overflow_is_flagged_not_an_error():
     """a_c = 8, u_z = 0, u_r = 5, u_c = 0.1: at the zero iterate the residual
     is z c~ = 0.5 tanh(0.1), about 0.05, and every Jacobian is about
