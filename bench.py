@@ -158,6 +158,23 @@ def _counter_rows(path, counter):
     return rows
 
 
+PMC_PREFIX = "rocprofv3 --pmc {counters} --output-format csv -d <out> -o run -- python3 <repo>/bench.py --workload {w} "
+
+
+def pmc_commands(workload: str, scan: bool) -> dict:
+    """The rocprofv3 counter runs whose CSVs the summaries below convert, as
+    run on the GPU machine (from /tmp with TMPDIR=/tmp), one run per counter set."""
+    extra = "" if scan else " --no-ceilings"
+    return {
+        "FETCH_SIZE": PMC_PREFIX.format(counters="FETCH_SIZE", w=workload)
+        + f"--steps 3 --warmup 1 --no-cpu-baseline{extra} --copy-calibration",
+        "WRITE_SIZE": PMC_PREFIX.format(counters="WRITE_SIZE", w=workload)
+        + f"--steps 3 --warmup 1 --no-cpu-baseline{extra} --copy-calibration",
+        "SQ": PMC_PREFIX.format(counters=" ".join(SQ_PASS), w=workload)
+        + "--steps 3 --warmup 1 --no-cpu-baseline --no-ceilings --no-per-iteration",
+    }
+
+
 def traffic_from_counters(workload: str, fetch_csv: str, write_csv: str, iters: int,
                           kernel: str = "newton_iter") -> dict:
     """Per-launch HBM bytes of one kernel from two rocprofv3 --pmc runs
@@ -196,11 +213,14 @@ def traffic_from_counters(workload: str, fetch_csv: str, write_csv: str, iters: 
     mean = sum(x["fetch"] + x["write"] for x in per_k) / iters
     return {"workload": workload, "kernel": f"{kernel}_kernel", "source_digest": source_digest(),
             "bytes_per_launch": mean, "per_launch": per_k, "fetch_scale": fscale, "write_scale": wscale,
-            "calibration": "1 GiB hipMemcpy device copy (__amd_rocclr_copyBuffer) in the same run"}
+            "calibration": "1 GiB hipMemcpy device copy (__amd_rocclr_copyBuffer) in the same run",
+            "commands": [c for n, c in pmc_commands(workload, kernel in ("scan", "dense")).items() if n != "SQ"]}
 
 
 # SQ counters of one --pmc pass: instruction counts are per wave (64 lanes).
 VALU_COUNTERS = ("SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32")
+SQ_PASS = VALU_COUNTERS + ("SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY",
+                           "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_ANY")
 
 
 def valu_from_counters(workload: str, csv_path: str, elements: int, iters: int, trans_in_valu: bool,
@@ -230,7 +250,8 @@ def valu_from_counters(workload: str, csv_path: str, elements: int, iters: int, 
             "regular_per_element_iteration": 64.0 * regular / (elements * iters),
             "trans_per_element_iteration": 64.0 * trans / (elements * iters),
             "slots_per_launch": slots, "slots_per_element_iteration": slots / (elements * iters),
-            "slot_rule": f"64 lanes x (regular VALU + {TRANS_SLOTS} x transcendental) wave instructions"}
+            "slot_rule": f"64 lanes x (regular VALU + {TRANS_SLOTS} x transcendental) wave instructions",
+            "command": pmc_commands(workload, False)["SQ"]}
 
 
 def write_stats_summary(workload: str, stats_csv: str, command: str) -> str:
