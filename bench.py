@@ -350,6 +350,29 @@ def stream_rates(dev, hip, L, n16=1 << 24):
     return res
 
 
+def issue_probe() -> int:
+    """The issue-rate kernels once each, for a counter pass: 768 workgroups
+    of 256 lanes (3 waves per SIMD on every SIMD), plain FMA chains (kind 0),
+    v_exp_f32 chains (kind 1) and the sigmoid-shaped mix (kind 2)."""
+    import torch
+
+    L = _ceil_lib()
+    if L is None:
+        print(json.dumps({"error": "libceilings.so is not built"}))
+        return 2
+    dev = torch.device("cuda:0")
+    blocks = 256 * 3
+    buf = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    for kind, iters in ((0, 200), (1, 100), (2, 100)):
+        if L.ceil_issue_launch(kind, blocks, iters, 0.999, 1e-3, ctypes.c_void_p(buf.data_ptr()), stream):
+            raise RuntimeError("ceil_issue_launch failed")
+        torch.cuda.synchronize()
+        print(json.dumps({"kind": kind, "lanes": blocks * 256, "steps_per_lane": iters * L.ceil_issue_steps_per_trip()}),
+              flush=True)
+    return 0
+
+
 def issue_rates(dev, hip, L, waves_per_simd=(1, 2, 3, 8)):
     """Lane operations per second of the issue-rate kernels, per waves per
     SIMD (all 256 CUs x 4 SIMDs filled): plain fp32 FMA, v_exp_f32, and the
@@ -826,7 +849,11 @@ def main(argv=None):
     ap.add_argument("--stats-summary", metavar="KERNEL_STATS_CSV",
                     help="write profiles/<workload>_kernel_stats.md from a rocprofv3 --stats CSV")
     ap.add_argument("--stats-command", default=None, help="the rocprofv3 command, for --stats-summary")
+    ap.add_argument("--issue-probe", action="store_true",
+                    help="launch the VALU issue-rate kernels once each (for a counter pass) and exit")
     args = ap.parse_args(argv)
+    if args.issue_probe:
+        return issue_probe()
     sys.path.insert(0, str(ROOT))
     from nonlinear_rnn_solve_newton_amd.workloads import DENSE_WORKLOADS, HEADLINE, SCAN_WORKLOADS, WORKLOADS
     name = args.workload or HEADLINE
